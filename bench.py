@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the AdaFuse pre-gate + one-launch fused merge on one MI355X.
+
+One step = ada_pregate (router GEMV + top-k + gates) -> ada_merge (every layer and
+projection, in place, one launch) -> ada_unmerge (one launch), on a seeded synthetic
+stack already resident in HBM.  The default workload is the Llama-2-7B-shaped stack
+with E=8 adapters of rank 16 per projection and top-2 gating (bf16).
+
+Prints one JSON line.  `value` is the whole step's algorithmic HBM bytes (W read and
+written by merge and by unmerge, the selected adapters read by each, the router read
+by pregate) divided by the measured step time.  `roofline` reports the merge kernel
+alone: algorithmic bytes per launch over its mean duration from HIP events recorded
+on the launch stream inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "full-model adapter merge: effective HBM GB/s (% of peak) and merge µs"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "merge_bf16_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_e8r16k2",
+                    help="preset: llama7b_e8r16k2 (default), llama7b_e16r64k4, llama70b_e8r16k2, tiny")
+    ap.add_argument("--out-of-place", action="store_true", help="merge into a separate W' buffer")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-copy-ceiling", action="store_true", help="skip the device copy measurement")
+    ap.add_argument("--cpu-sample-layers", type=int, default=1)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("merge.hip", "common.h"):
+        with open(os.path.join(ROOT, "weight_merge_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, mode: str):
+    """HBM bytes per merge launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel_sha") != kernel_sha() or rec.get("workload") != workload or rec.get("mode") != mode:
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+
+def copy_ceiling(torch, dev, gib=4.0, reps=10):
+    n = int(gib * (1 << 30)) // 2
+    a = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n * 2 / sec / 1e9
+
+
+def cpu_baseline(cfg, seed, n_layers):
+    """The fp64 NumPy oracle on a bounded sample of the same workload (the first
+    n_layers layers, drawn with the same generator), one step = pregate + merge +
+    unmerge, rated in the benchmark's unit."""
+    import numpy as np
+
+    from oracle import adafuse as O
+    from weight_merge_amd import synth
+    from weight_merge_amd.configs import scaled
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    sub = scaled(cfg, n_layers)
+    h, R = synth.router_inputs(cfg, seed)
+    st = synth.make_stack(sub, seed, device="cuda")  # same draws as the GPU stack's first layers
+    host = [[(st.W[l][p].double().cpu().numpy(), st.A[l][p].double().cpu().numpy(),
+              st.B[l][p].double().cpu().numpy()) for p in range(len(sub.projections))] for l in range(n_layers)]
+    del st
+    h64, R64 = h.double().numpy(), R.double().numpy()
+    t0 = time.perf_counter()
+    idx, g = O.pregate(h64, R64, cfg.k, cfg.renorm)
+    for layer in host:
+        for W, A, B in layer:
+            Wm = O.merge(W, A, B, idx, g, cfg.scale)
+            O.unmerge(Wm, A, B, idx, g, cfg.scale)
+    sec = time.perf_counter() - t0
+    step_bytes = 2 * sub.merge_bytes() + (cfg.E * cfg.d_model + cfg.d_model) * cfg.elem_bytes
+    return {
+        "value": round(step_bytes / sec / 1e9, 3),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"layers 0..{n_layers - 1} of {cfg.n_layers} ({n_layers * len(cfg.projections)} projections): "
+                  f"pregate + merge + unmerge in fp64 NumPy, {sec:.2f} s; inputs copied to host before timing",
+        "seconds": round(sec, 3),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the merge needs no communication and this build runs on a "
+              "single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from weight_merge_amd import api as A
+    from weight_merge_amd import synth
+    from weight_merge_amd.configs import PRESETS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 2
+        a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 2 * n, "bytes_written": 2 * n, "launches": 3}))
+        return
+
+    cfg = PRESETS[args.workload]
+    mode = "out_of_place" if args.out_of_place else "in_place"
+    t_gen = time.perf_counter()
+    st = synth.make_stack(cfg, args.seed, device=dev)
+    h, R = synth.router_inputs(cfg, args.seed)
+    h, R = h.to(dev), R.to(dev)
+    projs = []
+    for l, p, _ in st.items():
+        w = st.W[l][p]
+        projs.append((w, torch.empty_like(w) if args.out_of_place else None, st.A[l][p], st.B[l][p]))
+    model = A.AdaModel(projs, cfg.E, cfg.r)
+    idx = torch.empty(cfg.k, dtype=torch.int32, device=dev)
+    gate = torch.empty(cfg.k, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        A.ada_pregate(h, R, cfg.k, cfg.renorm, idx, gate)
+        if evs:
+            evs[1].record()
+        A.ada_merge(model, idx, gate, cfg.scale)
+        if evs:
+            evs[2].record()
+        A.ada_unmerge(model, idx, gate, cfg.scale)
+        if evs:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# workload {cfg.name}: {cfg.weight_elems() / 1e9:.2f}G weights, {model.tiles} tiles, "
+          f"generated in {gen_s:.1f}s; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    unmerge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    merge_bytes = cfg.merge_bytes()
+    pregate_bytes = (cfg.E * cfg.d_model + cfg.d_model) * cfg.elem_bytes
+    step_bytes = 2 * merge_bytes + pregate_bytes
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes * args.steps / wall / 1e9
+    merge_mean_s = sum(merge_ms) / len(merge_ms) / 1e3
+    achieved = merge_bytes / merge_mean_s / 1e9
+    traffic = read_traffic(cfg.name, mode)
+    n_tiles = model.tiles
+
+    ceiling = None if args.no_copy_ceiling else copy_ceiling(torch, dev)
+
+    del model, projs, st
+    torch.cuda.empty_cache()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.seed, args.cpu_sample_layers)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,.) draws on the device; no trained weights)",
+        "config": {
+            "workload": cfg.note,
+            "preset": cfg.name,
+            "layers": cfg.n_layers,
+            "E": cfg.E, "r": cfg.r, "k": cfg.k, "scale": cfg.scale,
+            "mode": mode,
+            "step": "pregate + merge + unmerge",
+            "weights_GB": round(cfg.weight_elems() * cfg.elem_bytes / 1e9, 3),
+            "merge_tiles": n_tiles,
+        },
+        "merge_us": {"mean": round(merge_mean_s * 1e6, 1), "median": round(pct(merge_ms, 0.5) * 1e3, 1),
+                     "min": round(min(merge_ms) * 1e3, 1), "p90": round(pct(merge_ms, 0.9) * 1e3, 1)},
+        "unmerge_us": {"median": round(pct(unmerge_ms, 0.5) * 1e3, 1), "min": round(min(unmerge_ms) * 1e3, 1)},
+        "pregate_us": {"median": round(pct(pre_ms, 0.5) * 1e3, 2), "min": round(min(pre_ms) * 1e3, 2)},
+        "merge_algorithmic_bytes": merge_bytes,
+        "merge_pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "copy_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
+        "merge_pct_of_copy_ceiling": None if ceiling is None else round(100 * achieved / ceiling, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "kernel": "merge_bf16_kernel" if cfg.dtype == "bf16" else "merge_f32_kernel",
+            "kernel_sha": kernel_sha(),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * adafuse.h -- C ABI of the AdaFuse pre-gating and fused adapter-merge library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (both summary pages of "AdaFuse: Accelerating Dynamic Adapter
+ * Inference via Token-Level Pre-Gating and Fused Kernel Optimization", cited here
+ * as [pt] for the Portuguese page and [ja] for the Japanese page):
+ *   - a single light router runs once on the leading token and picks the top-k
+ *     LoRA experts for every later layer ([pt] technical summary 2.A; [ja] 2.1);
+ *   - the picked adapters are fused into the backbone weights before decoding, in
+ *     one kernel call covering every layer ([pt] 2.B; [ja] 2.2), by concatenating
+ *     their down and up projections ([ja] 2.2);
+ *   - the fusion is undone, or switched to another selection, in one pass as well
+ *     ([pt] 2.B).
+ * Merged weights: W' = W + s * sum_j g_j * B_{e_j} A_{e_j}.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer unless stated otherwise, 16-byte
+ *     aligned, row-major, owned by the caller.  The library never allocates or
+ *     frees caller memory, and the hot calls (pregate, merge, unmerge, switch,
+ *     decode_gemv, lora_apply) allocate nothing at all.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     calls are asynchronous on that stream and return once the work is enqueued.
+ *   - Return value: ADA_OK (0) or a negative ada_status.  All argument checks run
+ *     on the host before any HIP call, so a rejected call has no effect.  A fault
+ *     inside a kernel surfaces at the caller's next synchronisation of the stream.
+ *   - dtype: ADA_F32 (fp32 storage) or ADA_BF16 (bf16 storage).  Gates are fp32
+ *     and every reduction accumulates in fp32; results are rounded to the storage
+ *     type once, to nearest-even.
+ *   - Dimensions d, d_in, d_out and row strides are counts of elements and must be
+ *     multiples of 8; 1 <= k <= E <= 64; k*r <= 512.
+ *   - LoRA layout: A (down) is [E][r][d_in], B (up) is [E][d_out][r], contiguous;
+ *     W is [d_out][ld_w] with ld_w >= d_in.
+ */
+#ifndef ADAFUSE_H
+#define ADAFUSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ADA_OK = 0,
+  ADA_EINVAL = -1,  /* null pointer, null or destroyed handle, bad flag value    */
+  ADA_ESHAPE = -2,  /* a size outside the supported range, or not a multiple of 8 */
+  ADA_EDTYPE = -3,  /* unknown dtype, or a dtype other than the model's           */
+  ADA_EALIGN = -4,  /* a pointer or row stride not 16-byte aligned                */
+  ADA_EHIP = -5,    /* a HIP runtime call or kernel launch failed                 */
+  ADA_ENOMEM = -6   /* the model's work table could not be allocated              */
+} ada_status;
+
+typedef enum { ADA_F32 = 0, ADA_BF16 = 1 } ada_dtype;
+
+/* One adapted projection: base weights and its bank of E LoRA adapters. */
+typedef struct {
+  void* w;          /* [d_out][ld_w] base weights                                */
+  void* w_out;      /* NULL or == w: merge in place; else [d_out][ld_w] output,    */
+                    /* written by merge, and the buffer unmerge/switch act on     */
+  const void* a;    /* [E][r][d_in] down projections                              */
+  const void* b;    /* [E][d_out][r] up projections                               */
+  int32_t d_out;
+  int32_t d_in;
+  int64_t ld_w;     /* row stride of w and w_out, elements                        */
+} ada_proj;
+
+typedef struct ada_model_s* ada_model;
+
+/*
+ * Register a stack of adapted projections (every layer and projection of a
+ * model, in any order).  Builds the per-projection work table the one-launch
+ * merge walks ([ja] 2.2: the large product is split into GEMM tiles assigned to
+ * thread blocks) and copies it to the current device; this is the only call that
+ * allocates (the table: ~64 bytes per projection plus a small tile index).
+ * n_proj >= 1; all projections share E, r and dtype.  On success *out owns the
+ * table until ada_model_destroy.  The registered pointers must stay valid, and
+ * may not be registered twice in one model.
+ */
+int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r,
+                     int32_t dtype, ada_model* out);
+
+/* Free the model's work table.  NULL is ignored.  Call after the model's last
+ * enqueued merge has completed. */
+void ada_model_destroy(ada_model m);
+
+/* Number of 128x128 output tiles one merge launch of this model covers (for
+ * measurement); negative status on a bad handle. */
+int64_t ada_model_tiles(ada_model m);
+
+/*
+ * Token-level pre-gating ([pt] 2.A; [ja] 2.1).  z = R h (fp32 accumulation);
+ * idx_out[0..k) = the k largest z in descending order, equal z lower index first;
+ * gate_out[j] = exp(z[idx_j] - z[idx_0]) / sum_i exp(z[idx_i] - z[idx_0]) when
+ * renorm = 1 (softmax over the selected logits), or the full softmax over all E
+ * logits read at idx_j when renorm = 0.  One workgroup; results stay on the
+ * device (idx_out, gate_out are device pointers) for the merge to read.
+ *   h: [d] hidden state of the leading token; router: [E][d]; dtype of both.
+ *   NaN logits give an unspecified (but in-range) selection.
+ */
+int ada_pregate(const void* h, const void* router, int32_t d, int32_t E, int32_t k,
+                int32_t dtype, int32_t renorm, int32_t* idx_out, float* gate_out,
+                void* stream);
+
+/*
+ * Fused merge of the selected adapters into every registered projection in ONE
+ * kernel launch ([pt] 2.B; [ja] 2.2):
+ *   w_out (or w in place) = RNE(w + sum_j scale*gate[j] * B[idx[j]] @ A[idx[j]]).
+ * idx, gate: device arrays of k entries (as written by ada_pregate).  Slots whose
+ * gate is 0 are skipped; if every gate is 0 an in-place merge writes nothing and
+ * an out-of-place merge copies w.  Indices outside [0, E) are skipped.  The
+ * caller keeps (idx, gate, scale) to unmerge.  Overlapping calls on one model's
+ * weights race.  k*r <= 512.
+ */
+int ada_merge(ada_model m, const int32_t* idx, const float* gate, int32_t k,
+              float scale, void* stream);
+
+/*
+ * De-fuse ([pt] 2.B): buffer = RNE(buffer - sum_j scale*gate[j] * B[idx[j]] @ A[idx[j]])
+ * on the merged buffer (w in place, or w_out for an out-of-place model), in one
+ * launch.  In bf16 this returns W to within rounding, not bit-exactly; repeated
+ * merge/unmerge cycles drift, so long-running callers restore from a pristine
+ * copy (or use an out-of-place model and simply merge again).
+ */
+int ada_unmerge(ada_model m, const int32_t* idx, const float* gate, int32_t k,
+                float scale, void* stream);
+
+/*
+ * Fused switch between selections ([pt] 2.B: undo the previous token's fusion and
+ * apply the current one in one pass): buffer = RNE(buffer - delta(prev) + delta(cur)),
+ * one read and one write of every weight.  (k_prev + k_cur) * r <= 512.
+ */
+int ada_switch(ada_model m, const int32_t* idx_prev, const float* gate_prev, int32_t k_prev,
+               const int32_t* idx_cur, const float* gate_cur, int32_t k_cur, float scale,
+               void* stream);
+
+/*
+ * Decode-step projection on the merged backbone ([pt] 2.B: after fusion, decoding
+ * runs with no routing): y[d_out] = RNE(w @ x), fp32 accumulation.
+ *   w: [d_out][ld_w]; x: [d_in]; y: [d_out]; all of `dtype`.
+ */
+int ada_decode_gemv(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w,
+                    const void* x, void* y, int32_t dtype, void* stream);
+
+/*
+ * One projection of the conventional, unmerged dynamic-adapter layer the pages
+ * compare against ([pt] technical summary 1; [ja] 1): y = RNE(w @ x + scale *
+ * sum_j gate[j] * B[idx[j]] (A[idx[j]] x)), computed as separate base-GEMV, shrink
+ * and expand kernels (three launches).  `workspace` is a caller-owned device
+ * buffer of at least (d_out + k*r) * 4 bytes for the fp32 intermediates.
+ */
+int ada_lora_apply(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w,
+                   const void* a, const void* b, int32_t E, int32_t r,
+                   const int32_t* idx, const float* gate, int32_t k, float scale,
+                   const void* x, void* y, void* workspace, int64_t workspace_bytes,
+                   int32_t dtype, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* ada_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAFUSE_H */

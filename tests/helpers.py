@@ -1,0 +1,85 @@
+"""Shared helpers of the test suite (test infrastructure: may call the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import adafuse as O
+from weight_merge_amd import synth
+
+# Merged bf16 weights: |W'_gpu - W'_ref| <= 8e-3 |W'_ref| + 1e-4, ref the unrounded
+# fp64 W + delta.  bf16 round-to-nearest alone costs <= 2^-8 |W'| (about half the
+# relative term); folding s*g into B in bf16 adds <= 2^-8 |delta| ~ 1e-6 absolute.
+BF16_RTOL, BF16_ATOL = 8e-3, 1e-4
+# fp32 storage: one final rounding (2^-24 relative) plus fp32 accumulation over k*r
+# terms; 1e-6 relative + 1e-7 absolute leaves a >10x margin and still catches a
+# dropped adapter (~5e-3).
+F32_RTOL, F32_ATOL = 1e-6, 1e-7
+# Gates: fp32 logits differ from fp64 by <~5e-5; the gate's relative error follows.
+GATE_RTOL, GATE_ATOL = 1e-4, 1e-6
+MIN_GAP = 1e-3
+
+
+def tol(dtype):
+    return (BF16_RTOL, BF16_ATOL) if dtype == torch.bfloat16 else (F32_RTOL, F32_ATOL)
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check_close(got: torch.Tensor | np.ndarray, ref: np.ndarray, rtol: float, atol: float, what: str = ""):
+    g = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    err = np.abs(g - ref)
+    bound = rtol * np.abs(ref) + atol
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; worst at {i}: "
+                             f"got {g[i]!r} ref {ref[i]!r} err {err[i]:.3e} bound {bound[i]:.3e}")
+    return float(np.max(err / (np.abs(ref) + atol / rtol))) if err.size else 0.0
+
+
+def min_gap(z) -> float:
+    s = np.sort(np.asarray(z, dtype=np.float64))
+    return float(np.min(np.diff(s))) if s.size > 1 else np.inf
+
+
+def gapped_router(E: int, d: int, dtype: str, seed: int):
+    """(h, R, seed) from the first seed at or after `seed` whose logits (per the
+    oracle) are pairwise at least 1e-3 apart, so top-k has no near-ties."""
+    s = seed
+    while True:
+        h, R = synth.small_router(s, E, d, dtype)
+        if min_gap(O.router_logits(to64(h), to64(R))) >= MIN_GAP:
+            return h, R, s
+        s += 1
+
+
+def gapped_stack_router(cfg, seed: int):
+    s = seed
+    while True:
+        h, R = synth.router_inputs(cfg, s)
+        if min_gap(O.router_logits(to64(h), to64(R))) >= MIN_GAP:
+            return h, R, s
+        s += 1
+
+
+def oracle_selection(h, R, k, renorm=True):
+    """Selection from the oracle, as device-ready int32 / fp32 tensors (plus the fp64
+    gates rounded to fp32, the exact values the kernel will read)."""
+    idx, g = O.pregate(to64(h), to64(R), k, renorm)
+    return torch.tensor(idx, dtype=torch.int32), torch.tensor(g, dtype=torch.float32)
+
+
+def sample_rows(d_out: int, rng: np.random.Generator, n_random: int = 24, tile: int = 128) -> np.ndarray:
+    """Rows covering every 16-row MFMA position of several tile bands: the first and
+    last row of 8 random bands, plus random rows, plus row 0 and the last row."""
+    n_bands = (d_out + tile - 1) // tile
+    bands = rng.choice(n_bands, size=min(8, n_bands), replace=False)
+    rows = {0, d_out - 1}
+    for b in bands:
+        rows.add(int(b) * tile)
+        rows.add(min(d_out, (int(b) + 1) * tile) - 1)
+    rows.update(int(v) for v in rng.integers(0, d_out, size=n_random))
+    return np.array(sorted(rows))

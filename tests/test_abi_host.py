@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before any
+HIP call (so these run without a GPU)."""
+import ctypes
+import os
+
+import pytest
+
+from weight_merge_amd import _lib
+from weight_merge_amd._lib import (ADA_BF16, ADA_EALIGN, ADA_EDTYPE, ADA_EINVAL, ADA_ESHAPE, ADA_F32,
+                                   AdaProj)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adafuse.h")
+
+# Fake, 16-byte aligned addresses: every call below fails validation before it
+# could touch them.
+P = 0x10000
+P2 = 0x20000
+MIS = 0x10004  # 4-byte but not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _lib.declared_functions(HEADER)
+    assert {"ada_pregate", "ada_merge", "ada_unmerge", "ada_decode_gemv"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(-6, 1):
+        assert lib.ada_status_string(s)
+    assert lib.ada_status_string(-99) == b"unknown status"
+
+
+def test_pregate_validation(lib):
+    f = lib.ada_pregate
+    ok = dict(h=P, router=P2, d=64, E=8, k=2, dt=ADA_BF16, renorm=1, idx=P, gate=P2)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["h"], a["router"], a["d"], a["E"], a["k"], a["dt"], a["renorm"], a["idx"], a["gate"], None)
+
+    assert call(h=None) == ADA_EINVAL
+    assert call(router=None) == ADA_EINVAL
+    assert call(idx=None) == ADA_EINVAL
+    assert call(gate=None) == ADA_EINVAL
+    assert call(dt=7) == ADA_EDTYPE
+    assert call(renorm=2) == ADA_EINVAL
+    assert call(h=MIS) == ADA_EALIGN
+    assert call(router=MIS) == ADA_EALIGN
+    assert call(idx=P + 2) == ADA_EALIGN
+    assert call(d=0) == ADA_ESHAPE
+    assert call(d=60) == ADA_ESHAPE      # not a multiple of 8
+    assert call(E=0) == ADA_ESHAPE
+    assert call(E=65) == ADA_ESHAPE
+    assert call(k=0) == ADA_ESHAPE
+    assert call(k=9) == ADA_ESHAPE       # k > E
+
+
+def proj(**kw):
+    a = dict(w=P, w_out=None, a=P2, b=P, d_out=256, d_in=256, ld_w=256)
+    a.update(kw)
+    return AdaProj(a["w"], a["w_out"], a["a"], a["b"], a["d_out"], a["d_in"], a["ld_w"])
+
+
+def create(lib, projs, E=4, r=8, dt=ADA_F32):
+    arr = (AdaProj * len(projs))(*projs)
+    h = ctypes.c_void_p()
+    st = lib.ada_model_create(arr, len(projs), E, r, dt, ctypes.byref(h))
+    assert h.value is None  # nothing allocated on failure
+    return st
+
+
+def test_model_create_validation(lib):
+    assert lib.ada_model_create(None, 1, 4, 8, ADA_F32, None) == ADA_EINVAL
+    arr = (AdaProj * 1)(proj())
+    assert lib.ada_model_create(arr, 1, 4, 8, ADA_F32, None) == ADA_EINVAL
+    assert create(lib, [proj()], dt=5) == ADA_EDTYPE
+    assert create(lib, [proj()], E=0) == ADA_ESHAPE
+    assert create(lib, [proj()], E=65) == ADA_ESHAPE
+    assert create(lib, [proj()], r=0) == ADA_ESHAPE
+    assert create(lib, [proj()], r=513) == ADA_ESHAPE
+    assert create(lib, [proj(w=None)]) == ADA_EINVAL
+    assert create(lib, [proj(a=None)]) == ADA_EINVAL
+    assert create(lib, [proj(b=None)]) == ADA_EINVAL
+    assert create(lib, [proj(w=MIS)]) == ADA_EALIGN
+    assert create(lib, [proj(w_out=MIS)]) == ADA_EALIGN
+    assert create(lib, [proj(a=MIS)]) == ADA_EALIGN
+    assert create(lib, [proj(d_out=100)]) == ADA_ESHAPE
+    assert create(lib, [proj(d_in=0)]) == ADA_ESHAPE
+    assert create(lib, [proj(ld_w=128)]) == ADA_ESHAPE   # ld < d_in
+    assert create(lib, [proj(d_in=8, ld_w=12)], dt=ADA_BF16) == ADA_EALIGN  # 24-byte rows
+    assert create(lib, [proj(), proj(d_out=1 << 23)]) == ADA_ESHAPE
+    arr0 = (AdaProj * 1)(proj())
+    h = ctypes.c_void_p()
+    assert lib.ada_model_create(arr0, 0, 4, 8, ADA_F32, ctypes.byref(h)) == ADA_ESHAPE
+
+
+def test_merge_calls_reject_bad_handles(lib):
+    fake = ctypes.c_void_p(P)  # not a model: the magic check must reject it...
+    # ...but reading through a wild pointer is not safe, so only NULL is probed here;
+    # a live model's checks are exercised on the GPU.
+    del fake
+    assert lib.ada_merge(None, P, P2, 2, 2.0, None) == ADA_EINVAL
+    assert lib.ada_unmerge(None, P, P2, 2, 2.0, None) == ADA_EINVAL
+    assert lib.ada_switch(None, P, P2, 2, P, P2, 2, 2.0, None) == ADA_EINVAL
+    assert lib.ada_model_tiles(None) == ADA_EINVAL
+    lib.ada_model_destroy(None)
+
+
+def test_gemv_validation(lib):
+    f = lib.ada_decode_gemv
+    assert f(None, 64, 64, 64, P, P2, ADA_BF16, None) == ADA_EINVAL
+    assert f(P, 64, 64, 64, None, P2, ADA_BF16, None) == ADA_EINVAL
+    assert f(P, 64, 64, 64, P, None, ADA_BF16, None) == ADA_EINVAL
+    assert f(P, 64, 64, 64, P, P2, 9, None) == ADA_EDTYPE
+    assert f(MIS, 64, 64, 64, P, P2, ADA_BF16, None) == ADA_EALIGN
+    assert f(P, 60, 64, 64, P, P2, ADA_BF16, None) == ADA_ESHAPE
+    assert f(P, 64, 64, 32, P, P2, ADA_BF16, None) == ADA_ESHAPE
+    assert f(P, 64, 64, 68, P, P2, ADA_BF16, None) == ADA_EALIGN
+
+
+def test_lora_apply_validation(lib):
+    f = lib.ada_lora_apply
+    base = [P, 64, 64, 64, P2, P, 4, 8, P, P2, 2, 2.0, P, P2, P, (64 + 16) * 4, ADA_BF16, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(0, None) == ADA_EINVAL
+    assert call(14, None) == ADA_EINVAL
+    assert call(16, 3) == ADA_EDTYPE
+    assert call(14, MIS) == ADA_EALIGN
+    assert call(8, P + 2) == ADA_EALIGN
+    assert call(1, 7) == ADA_ESHAPE
+    assert call(6, 0) == ADA_ESHAPE    # E
+    assert call(10, 5) == ADA_ESHAPE   # k > E
+    assert call(15, 64 * 4) == ADA_ESHAPE  # workspace too small

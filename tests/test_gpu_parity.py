@@ -1,0 +1,381 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by
+element, on seeded inputs that span several tiles and ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import (GATE_ATOL, GATE_RTOL, check_close, gapped_router, min_gap, oracle_selection, to64,
+                     tol)
+from oracle import adafuse as O
+from weight_merge_amd import api as A
+from weight_merge_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- pre-gating
+
+PREGATE_CASES = [
+    # E, k, d, dtype, renorm
+    (4, 2, 256, "fp32", True),
+    (8, 2, 4096, "bf16", True),
+    (16, 4, 4096, "bf16", True),
+    (8, 2, 8192, "bf16", True),
+    (1, 1, 8, "bf16", True),
+    (2, 2, 16, "fp32", True),
+    (64, 8, 1032, "bf16", True),
+    (64, 64, 520, "fp32", True),
+    (33, 5, 264, "bf16", False),
+    (16, 4, 4096, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("E,k,d,dt,renorm", PREGATE_CASES)
+def test_pregate_matches_oracle(E, k, d, dt, renorm):
+    for seed in (11, 12, 13):
+        h, R, _ = gapped_router(E, d, dt, seed * 1000)
+        idx, gate = A.ada_pregate(h.to(DEV), R.to(DEV), k, renorm=renorm)
+        sync()
+        ridx, rg = O.pregate(to64(h), to64(R), k, renorm)
+        assert idx.cpu().numpy().tolist() == ridx.tolist(), (seed, E, k, d)
+        check_close(gate, rg, GATE_RTOL, GATE_ATOL, "gates")
+
+
+def test_pregate_ties_go_to_the_lower_index():
+    # identical router rows give identical logits (same summation order per row)
+    E, d = 8, 512
+    h, R, _ = gapped_router(E, d, "bf16", 5)
+    R[5] = R[2]
+    R[7] = R[2]
+    z = O.router_logits(to64(h), to64(R))
+    top = int(np.argmax(z))
+    idx, gate = A.ada_pregate(h.to(DEV), R.to(DEV), E)
+    sync()
+    got = idx.cpu().tolist()
+    assert got == O.select_topk(z, E).tolist()
+    assert got.index(2) < got.index(5) < got.index(7)
+    assert top in got
+
+
+# ---------------------------------------------------------------- merge
+
+MERGE_CASES = [
+    # E, r, k, d_out, d_in, dtype, inplace
+    (4, 8, 2, 256, 256, "fp32", True),
+    (5, 3, 2, 40, 48, "fp32", False),
+    (8, 16, 2, 384, 520, "bf16", False),
+    (8, 16, 2, 136, 1000, "bf16", True),
+    (16, 64, 4, 136, 264, "bf16", True),
+    (8, 4, 3, 200, 72, "bf16", False),
+    (6, 12, 2, 128, 128, "bf16", True),
+    (64, 8, 64, 96, 40, "bf16", False),
+    (1, 16, 1, 8, 8, "bf16", True),
+    (16, 128, 4, 264, 1032, "bf16", True),
+    (3, 1, 3, 24, 16, "bf16", False),
+]
+
+
+def make_selection(E, k, d, dt, seed):
+    h, R, _ = gapped_router(E, d, dt, seed)
+    return oracle_selection(h, R, k)
+
+
+@pytest.mark.parametrize("E,r,k,d_out,d_in,dt,inplace", MERGE_CASES)
+def test_merge_matches_oracle(E, r, k, d_out, d_in, dt, inplace):
+    W, Aw, Bw = synth.adapter_bank(7, E, r, d_out, d_in, dt)
+    idx, gate = make_selection(E, k, 64, dt, 3)
+    s = 2.0
+    ref = O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64), s)
+    w = W.to(DEV)
+    out = None if inplace else torch.full_like(w, float("nan"))
+    m = A.AdaModel([(w, out, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), s)
+    sync()
+    got = w if inplace else out
+    check_close(got, ref, *tol(TD[dt]), "merge")
+    if not inplace:
+        assert torch.equal(w.cpu(), W), "out-of-place merge must not write W"
+
+
+def test_stack_of_mixed_shapes_in_one_launch():
+    """Several projections of different shapes in one model (one launch): every
+    projection gets its own adapters and the same selection."""
+    E, r, k, dt = 8, 16, 2, "bf16"
+    shapes = [(256, 256), (64, 256), (688, 256), (256, 688), (8, 8), (136, 1000)] * 2
+    banks = [synth.adapter_bank(100 + i, E, r, do, di, dt) for i, (do, di) in enumerate(shapes)]
+    idx, gate = make_selection(E, k, 256, dt, 9)
+    dev = [(W.to(DEV), None, Aw.to(DEV), Bw.to(DEV)) for W, Aw, Bw in banks]
+    m = A.AdaModel(dev, E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    for (W, Aw, Bw), (w, _, _, _) in zip(banks, dev):
+        ref = O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64), 2.0)
+        check_close(w, ref, *tol(torch.bfloat16), f"merge {tuple(W.shape)}")
+
+
+def test_row_strided_weights():
+    """W with a row stride larger than d_in (a column slice of a wider matrix)."""
+    E, r, k = 8, 16, 2
+    big, Aw, Bw = synth.adapter_bank(21, E, r, 264, 512, "bf16")
+    W = big[:, :392]  # ld 512, d_in 392
+    Aw = Aw[:, :, :392].contiguous()
+    idx, gate = make_selection(E, k, 64, "bf16", 4)
+    ref = O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64), 2.0)
+    wbig = big.to(DEV)
+    w = wbig[:, :392]
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    check_close(w, ref, *tol(torch.bfloat16), "strided merge")
+    assert torch.equal(wbig[:, 392:].cpu(), big[:, 392:]), "columns past d_in must stay untouched"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_zero_gates_leave_w_bit_identical(dt):
+    E, r, k = 4, 16, 2
+    W, Aw, Bw = synth.adapter_bank(31, E, r, 200, 264, dt)
+    W[0, :8] = -0.0
+    w = W.to(DEV)
+    out = torch.full_like(w, float("nan"))
+    idx = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
+    gate = torch.zeros(2, dtype=torch.float32, device=DEV)
+    m_in = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    m_out = A.AdaModel([(w, out, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m_in, idx, gate, 2.0)
+    A.ada_merge(m_out, idx, gate, 2.0)
+    sync()
+    assert w.cpu().view(torch.int16 if dt == "bf16" else torch.int32).equal(
+        W.view(torch.int16 if dt == "bf16" else torch.int32))
+    assert out.cpu().view(torch.int16 if dt == "bf16" else torch.int32).equal(
+        W.view(torch.int16 if dt == "bf16" else torch.int32))
+
+
+def test_zero_gated_slot_is_dropped():
+    E, r = 4, 16
+    W, Aw, Bw = synth.adapter_bank(32, E, r, 128, 128, "bf16")
+    Aw[1, 0, 5] = float("inf")
+    idx = torch.tensor([1, 2], dtype=torch.int32)
+    gate = torch.tensor([0.0, 0.7], dtype=torch.float32)
+    ref = O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64), 2.0)
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    assert torch.isfinite(w).all()
+    check_close(w, ref, *tol(torch.bfloat16), "zero-gated slot")
+
+
+def test_single_expert_unit_gate_is_static_lora():
+    E, r = 3, 16
+    W, Aw, Bw = synth.adapter_bank(33, E, r, 256, 384, "bf16")
+    ref = to64(W) + 2.0 * to64(Bw[2]) @ to64(Aw[2])
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m, torch.tensor([2], dtype=torch.int32, device=DEV), torch.ones(1, device=DEV), 2.0)
+    sync()
+    check_close(w, ref, *tol(torch.bfloat16), "k=1 static merge")
+
+
+def test_out_of_range_index_is_skipped():
+    E, r = 4, 8
+    W, Aw, Bw = synth.adapter_bank(34, E, r, 64, 64, "bf16")
+    idx = torch.tensor([7, 1], dtype=torch.int32)
+    gate = torch.tensor([0.5, 0.5], dtype=torch.float32)
+    ref = O.merge(to64(W), to64(Aw), to64(Bw), [1], [0.5], 2.0)
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    check_close(w, ref, *tol(torch.bfloat16), "out-of-range slot")
+
+
+# ---------------------------------------------------------------- unmerge / switch
+
+
+@pytest.mark.parametrize("dt,E,r,k", [("bf16", 8, 16, 2), ("bf16", 16, 64, 4), ("fp32", 4, 8, 2)])
+def test_unmerge_matches_oracle(dt, E, r, k):
+    W, Aw, Bw = synth.adapter_bank(41, E, r, 264, 392, dt)
+    idx, gate = make_selection(E, k, 64, dt, 5)
+    ref = O.unmerge(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64), 2.0)
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_unmerge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    check_close(w, ref, *tol(TD[dt]), "unmerge")
+
+
+@pytest.mark.parametrize("inplace", [True, False])
+def test_merge_then_unmerge_returns_w(inplace):
+    E, r, k = 8, 16, 2
+    W, Aw, Bw = synth.adapter_bank(42, E, r, 520, 392, "bf16")
+    idx, gate = make_selection(E, k, 64, "bf16", 6)
+    w = W.to(DEV)
+    out = None if inplace else torch.empty_like(w)
+    m = A.AdaModel([(w, out, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    A.ada_unmerge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    buf = w if inplace else out
+    check_close(buf, to64(W), *tol(torch.bfloat16), "merge->unmerge")
+    # bf16 subtraction does not undo bf16 addition exactly; the bit-exact fraction
+    # must match two round-to-nearest steps simulated on the oracle's delta
+    delta = O.adapter_delta(to64(Aw), to64(Bw), idx.numpy(), 2.0 * gate.numpy().astype(np.float64))
+    w1 = torch.from_numpy(to64(W) + delta).to(torch.bfloat16)
+    w2 = torch.from_numpy(to64(w1) - delta).to(torch.bfloat16)
+    expect = (w2.view(torch.int16) == W.view(torch.int16)).float().mean().item()
+    exact = (buf.cpu().view(torch.int16) == W.view(torch.int16)).float().mean().item()
+    assert exact >= expect - 0.02, (exact, expect)
+    if not inplace:
+        assert torch.equal(w.cpu(), W)
+
+
+def test_switch_matches_oracle():
+    E, r = 8, 16
+    W, Aw, Bw = synth.adapter_bank(43, E, r, 264, 520, "bf16")
+    pi, pg = make_selection(E, 2, 64, "bf16", 7)
+    ci, cg = make_selection(E, 3, 64, "bf16", 8)
+    ref = O.switch(to64(W), to64(Aw), to64(Bw), (pi.numpy(), pg.numpy().astype(np.float64)),
+                   (ci.numpy(), cg.numpy().astype(np.float64)), 2.0)
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_switch(m, (pi.to(DEV), pg.to(DEV)), (ci.to(DEV), cg.to(DEV)), 2.0)
+    sync()
+    check_close(w, ref, *tol(torch.bfloat16), "switch")
+
+
+# ---------------------------------------------------------------- invariants
+
+
+def test_merge_is_deterministic():
+    E, r, k = 16, 64, 4
+    W, Aw, Bw = synth.adapter_bank(51, E, r, 392, 520, "bf16")
+    idx, gate = make_selection(E, k, 64, "bf16", 9)
+    w = W.to(DEV)
+    o1, o2 = torch.empty_like(w), torch.empty_like(w)
+    a, b = Aw.to(DEV), Bw.to(DEV)
+    m1 = A.AdaModel([(w, o1, a, b)], E, r)
+    m2 = A.AdaModel([(w, o2, a, b)], E, r)
+    A.ada_merge(m1, idx.to(DEV), gate.to(DEV), 2.0)
+    A.ada_merge(m2, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_expert_relabelling_is_bit_identical():
+    """Permute the adapter banks together with the router rows: the GPU selects the
+    permuted experts in the same order and writes bit-identical weights."""
+    E, r, k, d = 8, 16, 2, 256
+    W, Aw, Bw = synth.adapter_bank(52, E, r, 256, 256, "bf16")
+    h, R, _ = gapped_router(E, d, "bf16", 77)
+    perm = torch.tensor(np.random.default_rng(0).permutation(E))
+    outs = []
+    for P in (torch.arange(E), perm):
+        w = W.to(DEV)
+        idx, gate = A.ada_pregate(h.to(DEV), R[P].contiguous().to(DEV), k)
+        m = A.AdaModel([(w, None, Aw[P].contiguous().to(DEV), Bw[P].contiguous().to(DEV))], E, r)
+        A.ada_merge(m, idx, gate, 2.0)
+        sync()
+        outs.append((w.cpu(), P[idx.cpu().long()]))
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+
+
+def test_pregate_then_merge_chain():
+    """GPU pregate feeding GPU merge (no host round trip) vs oracle pregate + merge."""
+    E, r, k, d = 16, 64, 4, 1024
+    W, Aw, Bw = synth.adapter_bank(53, E, r, 264, 1024, "bf16")
+    h, R, _ = gapped_router(E, d, "bf16", 99)
+    ridx, rg = O.pregate(to64(h), to64(R), k)
+    ref = O.merge(to64(W), to64(Aw), to64(Bw), ridx, rg, 2.0)
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    idx, gate = A.ada_pregate(h.to(DEV), R.to(DEV), k)
+    A.ada_merge(m, idx, gate, 2.0)
+    sync()
+    check_close(w, ref, *tol(torch.bfloat16), "pregate->merge")
+
+
+# ---------------------------------------------------------------- decode GEMV and baseline
+
+GEMV_CASES = [(4096, 4096, "bf16"), (11008, 4096, "bf16"), (4096, 11008, "bf16"), (8, 8, "bf16"),
+              (264, 1000, "bf16"), (256, 256, "fp32"), (520, 72, "fp32"), (1024, 8192, "bf16")]
+
+
+def gemv_bound(W64, x64, y_ref, dt):
+    mag = np.abs(W64) @ np.abs(x64)
+    if dt == "bf16":
+        return 8e-3 * np.abs(y_ref) + 1e-4 * mag
+    return 1e-6 * np.abs(y_ref) + 1e-5 * mag
+
+
+@pytest.mark.parametrize("d_out,d_in,dt", GEMV_CASES)
+def test_decode_gemv_matches_oracle(d_out, d_in, dt):
+    W, _, _ = synth.adapter_bank(61, 1, 8, d_out, d_in, dt)
+    x = synth.host_normal(synth.tensor_seed(62, d_in), (d_in,), 1.0, dt)
+    y = A.ada_decode_gemv(W.to(DEV), x.to(DEV))
+    sync()
+    W64, x64 = to64(W), to64(x)
+    ref = O.gemv(W64, x64)
+    err = np.abs(to64(y) - ref)
+    assert np.all(err <= gemv_bound(W64, x64, ref, dt)), float(err.max())
+
+
+@pytest.mark.parametrize("dt,E,r,k", [("bf16", 8, 16, 2), ("bf16", 16, 64, 4), ("fp32", 4, 8, 2)])
+def test_lora_apply_matches_oracle(dt, E, r, k):
+    d_out, d_in = 1032, 520
+    W, Aw, Bw = synth.adapter_bank(63, E, r, d_out, d_in, dt)
+    x = synth.host_normal(synth.tensor_seed(64, d_in), (d_in,), 1.0, dt)
+    idx, gate = make_selection(E, k, 64, dt, 10)
+    y = A.ada_lora_apply(W.to(DEV), Aw.to(DEV), Bw.to(DEV), idx.to(DEV), gate.to(DEV), 2.0, x.to(DEV))
+    sync()
+    ref = O.routed_lora_forward(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64),
+                                2.0, to64(x))
+    W64, x64 = to64(W), to64(x)
+    mag = np.abs(W64) @ np.abs(x64)
+    err = np.abs(to64(y) - ref)
+    assert np.all(err <= gemv_bound(W64, x64, ref, dt) + 1e-4 * mag), float(err.max())
+
+
+def test_merged_decode_equals_routed_baseline():
+    """Linearity through bf16 rounding: GEMV on the merged weights vs the unmerged
+    routed projection, relative L2 within 5e-3 (a dropped adapter gives ~4%)."""
+    E, r, k = 8, 16, 2
+    W, Aw, Bw = synth.adapter_bank(65, E, r, 4096, 4096, "bf16")
+    x = synth.host_normal(synth.tensor_seed(66, 4096), (4096,), 1.0, "bf16").to(DEV)
+    idx, gate = make_selection(E, k, 64, "bf16", 11)
+    w = W.to(DEV)
+    a, b = Aw.to(DEV), Bw.to(DEV)
+    y_base = A.ada_lora_apply(w, a, b, idx.to(DEV), gate.to(DEV), 2.0, x)
+    m = A.AdaModel([(w, None, a, b)], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    y_m = A.ada_decode_gemv(w, x)
+    sync()
+    yb, ym = to64(y_base), to64(y_m)
+    rel = np.linalg.norm(ym - yb) / np.linalg.norm(yb)
+    assert rel <= 5e-3, rel
+
+
+# ---------------------------------------------------------------- API errors on a live model
+
+
+def test_live_model_rejects_bad_selections():
+    E, r = 4, 128
+    W, Aw, Bw = synth.adapter_bank(71, E, r, 64, 64, "bf16")
+    m = A.AdaModel([(W.to(DEV), None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    idx = torch.zeros(4, dtype=torch.int32, device=DEV)
+    gate = torch.zeros(4, dtype=torch.float32, device=DEV)
+    with pytest.raises(A.AdaError) as ei:
+        A.ada_merge(m, idx, gate, 2.0)  # k*r = 512 is fine
+        A.ada_switch(m, (idx, gate), (idx, gate), 2.0)  # 8*128 > 512
+    assert ei.value.status == -2
+    with pytest.raises(A.AdaError):
+        A.ada_merge(m, idx[:0], gate[:0], 2.0)
+    m.destroy()
+    with pytest.raises(RuntimeError):
+        A.ada_merge(m, idx, gate, 2.0)

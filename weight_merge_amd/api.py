@@ -1,0 +1,198 @@
+"""Python binding of libadafuse: argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI; this module turns torch
+tensors (device memory) and the current torch stream into the pointers and sizes the
+C calls take, and turns negative status codes into exceptions.  Output tensors a
+caller does not pass are allocated here with torch, outside the C calls.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import ADA_BF16, ADA_F32, AdaProj
+
+_DT = {torch.float32: ADA_F32, torch.bfloat16: ADA_BF16}
+
+
+class AdaError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = _lib.load().ada_status_string(status).decode()
+        super().__init__(f"{call} failed with status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise AdaError(status, call)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16") from None
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def ada_pregate(h: torch.Tensor, router: torch.Tensor, k: int, renorm: bool = True,
+                idx_out: torch.Tensor | None = None, gate_out: torch.Tensor | None = None,
+                stream=None):
+    """Router GEMV + top-k + gates (one kernel).  Returns (idx int32[k], gate fp32[k])
+    on the device."""
+    _contig(h, "h")
+    _contig(router, "router")
+    E, d = router.shape
+    if h.shape != (d,) or h.dtype != router.dtype:
+        raise ValueError("h must be [d] with the router's dtype")
+    if idx_out is None:
+        idx_out = torch.empty(k, dtype=torch.int32, device=h.device)
+    if gate_out is None:
+        gate_out = torch.empty(k, dtype=torch.float32, device=h.device)
+    st = _lib.load().ada_pregate(_dev(h, "h"), _dev(router, "router"), d, E, k, _dtype(h), int(bool(renorm)),
+                                 _dev(idx_out, "idx_out"), _dev(gate_out, "gate_out"), _stream(stream))
+    _check(st, "ada_pregate")
+    return idx_out, gate_out
+
+
+class AdaModel:
+    """A registered stack of adapted projections (owns the device work table).
+
+    projs: iterable of (w, w_out, a, b) with w [d_out, d_in] (row stride w.stride(0)),
+    w_out None (merge in place) or a tensor like w, a [E, r, d_in], b [E, d_out, r].
+    The tensors must outlive the model; the model keeps references to them.
+    """
+
+    def __init__(self, projs, E: int, r: int):
+        projs = list(projs)
+        if not projs:
+            raise ValueError("no projections")
+        dt = projs[0][0].dtype
+        arr = (AdaProj * len(projs))()
+        keep = []
+        for i, (w, w_out, a, b) in enumerate(projs):
+            d_out, d_in = w.shape
+            if w.stride(1) != 1 or (w_out is not None and (w_out.shape != w.shape or w_out.stride() != w.stride())):
+                raise ValueError("w must have unit column stride; w_out must match w's layout")
+            _contig(a, "a")
+            _contig(b, "b")
+            if a.shape != (E, r, d_in) or b.shape != (E, d_out, r):
+                raise ValueError(f"adapter bank shapes {tuple(a.shape)}, {tuple(b.shape)} do not match "
+                                 f"E={E}, r={r}, W {tuple(w.shape)}")
+            for t in (w, a, b) + ((w_out,) if w_out is not None else ()):
+                if t.dtype != dt:
+                    raise TypeError("all tensors of a model share one dtype")
+            arr[i] = AdaProj(_dev(w, "w"), _dev(w_out, "w_out") if w_out is not None else None,
+                             _dev(a, "a"), _dev(b, "b"), d_out, d_in, w.stride(0))
+            keep.append((w, w_out, a, b))
+        handle = ctypes.c_void_p()
+        st = _lib.load().ada_model_create(arr, len(projs), E, r, _DT[dt], ctypes.byref(handle))
+        _check(st, "ada_model_create")
+        self._h = handle
+        self._keep = keep
+        self.E, self.r, self.dtype = E, r, dt
+        self.n_proj = len(projs)
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("model destroyed")
+        return self._h
+
+    @property
+    def tiles(self) -> int:
+        return int(_lib.load().ada_model_tiles(self.handle))
+
+    def destroy(self):
+        if getattr(self, "_h", None) is not None:
+            _lib.load().ada_model_destroy(self._h)
+            self._h = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def _sel(idx: torch.Tensor, gate: torch.Tensor):
+    if idx.dtype != torch.int32 or gate.dtype != torch.float32:
+        raise TypeError("idx must be int32 and gate float32")
+    if idx.numel() != gate.numel():
+        raise ValueError("idx and gate must have the same length")
+    return _dev(idx, "idx"), _dev(gate, "gate"), idx.numel()
+
+
+def ada_merge(model: AdaModel, idx: torch.Tensor, gate: torch.Tensor, scale: float, stream=None):
+    """Fuse the selected adapters into every registered projection (one launch)."""
+    pi, pg, k = _sel(idx, gate)
+    _check(_lib.load().ada_merge(model.handle, pi, pg, k, float(scale), _stream(stream)), "ada_merge")
+
+
+def ada_unmerge(model: AdaModel, idx: torch.Tensor, gate: torch.Tensor, scale: float, stream=None):
+    """De-fuse the selection from the merged buffer (one launch)."""
+    pi, pg, k = _sel(idx, gate)
+    _check(_lib.load().ada_unmerge(model.handle, pi, pg, k, float(scale), _stream(stream)), "ada_unmerge")
+
+
+def ada_switch(model: AdaModel, prev, cur, scale: float, stream=None):
+    """Undo selection `prev` and apply `cur` in one pass; prev, cur = (idx, gate)."""
+    pi, pg, pk = _sel(*prev)
+    ci, cg, ck = _sel(*cur)
+    _check(_lib.load().ada_switch(model.handle, pi, pg, pk, ci, cg, ck, float(scale), _stream(stream)),
+           "ada_switch")
+
+
+def ada_decode_gemv(w: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None, stream=None):
+    """y = W x on the device (fp32 accumulation, one rounding)."""
+    d_out, d_in = w.shape
+    if w.stride(1) != 1:
+        raise ValueError("w must have unit column stride")
+    _contig(x, "x")
+    if x.shape != (d_in,) or x.dtype != w.dtype:
+        raise ValueError("x must be [d_in] with w's dtype")
+    if y is None:
+        y = torch.empty(d_out, dtype=w.dtype, device=w.device)
+    st = _lib.load().ada_decode_gemv(_dev(w, "w"), d_out, d_in, w.stride(0), _dev(x, "x"), _dev(y, "y"),
+                                     _dtype(w), _stream(stream))
+    _check(st, "ada_decode_gemv")
+    return y
+
+
+def ada_lora_apply(w, a, b, idx, gate, scale: float, x, y=None, workspace=None, stream=None):
+    """Unmerged routed projection y = W x + s sum_j g_j B_j (A_j x) (three launches)."""
+    d_out, d_in = w.shape
+    E, r, _ = a.shape
+    pi, pg, k = _sel(idx, gate)
+    if y is None:
+        y = torch.empty(d_out, dtype=w.dtype, device=w.device)
+    need = (d_out + k * r) * 4
+    if workspace is None:
+        workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=w.device)
+    st = _lib.load().ada_lora_apply(_dev(w, "w"), d_out, d_in, w.stride(0), _dev(a, "a"), _dev(b, "b"),
+                                    E, r, pi, pg, k, float(scale), _dev(x, "x"), _dev(y, "y"),
+                                    _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                    _dtype(w), _stream(stream))
+    _check(st, "ada_lora_apply")
+    return y

@@ -1,0 +1,267 @@
+// C ABI of libadafuse: argument checks (host only, before any HIP call), the
+// per-model work table, and kernel launches.  The operations themselves are
+// documented in include/adafuse.h and in the kernel sources.
+#include "adafuse.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+constexpr uint64_t kModelMagic = 0x6164614675736521ull;
+constexpr int64_t kMaxDim = int64_t(1) << 22;     // rows or columns of one projection
+constexpr int64_t kMaxTiles = (int64_t(1) << 24) - 1;  // one grid: tiles * 256 threads < 2^32
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool dim_ok(int64_t d) { return d > 0 && d % 8 == 0 && d <= kMaxDim; }
+bool dtype_ok(int32_t dt) { return dt == ADA_F32 || dt == ADA_BF16; }
+
+}  // namespace
+
+struct ada_model_s {
+  uint64_t magic;
+  int32_t dtype;
+  int32_t E;
+  int32_t r;
+  int32_t n_proj;
+  int32_t lut_shift;
+  int32_t device;
+  int64_t total_tiles;
+  void* dev;                      // one allocation: entries, then the lookup table
+  const ada::MergeEntry* entries;
+  const int32_t* lut;
+};
+
+namespace {
+
+bool model_ok(const ada_model_s* m) { return m != nullptr && m->magic == kModelMagic; }
+
+int launch_merge_common(ada_model m, const ada::Selection& s0, const ada::Selection& s1,
+                        int src_is_out, int kr_max, void* stream) {
+  ada::MergeParams p{};
+  p.table = m->entries;
+  p.lut = m->lut;
+  p.total_tiles = m->total_tiles;
+  p.lut_shift = m->lut_shift;
+  p.n_entries = m->n_proj;
+  p.sel[0] = s0;
+  p.sel[1] = s1;
+  p.E = m->E;
+  p.r = m->r;
+  p.src_is_out = src_is_out;
+  p.xcd_remap = 1;
+  const hipError_t e = ada::launch_merge(p, m->dtype, kr_max, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : ADA_EHIP;
+}
+
+int check_selection(const ada_model_s* m, const int32_t* idx, const float* gate, int32_t k) {
+  if (idx == nullptr || gate == nullptr) return ADA_EINVAL;
+  if (!aligned4(idx) || !aligned4(gate)) return ADA_EALIGN;
+  if (k < 1 || k > m->E) return ADA_ESHAPE;
+  return ADA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ada_status_string(int status) {
+  switch (status) {
+    case ADA_OK: return "ok";
+    case ADA_EINVAL: return "invalid argument (null pointer, bad handle or flag)";
+    case ADA_ESHAPE: return "unsupported size (dimensions must be positive multiples of 8; 1<=k<=E<=64; k*r<=512)";
+    case ADA_EDTYPE: return "unsupported or mismatched dtype";
+    case ADA_EALIGN: return "pointer or row stride not 16-byte aligned";
+    case ADA_EHIP: return "HIP runtime call or kernel launch failed";
+    case ADA_ENOMEM: return "device allocation of the work table failed";
+    default: return "unknown status";
+  }
+}
+
+int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r, int32_t dtype,
+                     ada_model* out) {
+  if (out == nullptr || projs == nullptr) return ADA_EINVAL;
+  *out = nullptr;
+  if (!dtype_ok(dtype)) return ADA_EDTYPE;
+  if (n_proj < 1 || n_proj > (1 << 20)) return ADA_ESHAPE;
+  if (E < 1 || E > 64 || r < 1 || r > ada::kMaxKR) return ADA_ESHAPE;
+  const int tile = dtype == ADA_BF16 ? ada::kTileBF16 : ada::kTileF32;
+  const int esz = dtype == ADA_BF16 ? 2 : 4;
+
+  std::vector<ada::MergeEntry> ent(static_cast<size_t>(n_proj) + 1);
+  int64_t total = 0, min_tiles = INT64_MAX;
+  for (int32_t i = 0; i < n_proj; ++i) {
+    const ada_proj& p = projs[i];
+    if (p.w == nullptr || p.a == nullptr || p.b == nullptr) return ADA_EINVAL;
+    if (!aligned16(p.w) || !aligned16(p.a) || !aligned16(p.b) ||
+        (p.w_out != nullptr && !aligned16(p.w_out)))
+      return ADA_EALIGN;
+    if (!dim_ok(p.d_out) || !dim_ok(p.d_in)) return ADA_ESHAPE;
+    if (p.ld_w < p.d_in || p.ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
+    if ((p.ld_w * esz) % 16 != 0) return ADA_EALIGN;
+    const int64_t tm = (p.d_out + tile - 1) / tile, tn = (p.d_in + tile - 1) / tile;
+    ada::MergeEntry& e = ent[i];
+    e.w = p.w;
+    e.w_out = p.w_out != nullptr ? p.w_out : p.w;
+    e.a = p.a;
+    e.b = p.b;
+    e.ld = p.ld_w;
+    e.d_out = p.d_out;
+    e.d_in = p.d_in;
+    e.tiles_n = static_cast<int32_t>(tn);
+    e.tiles_m = static_cast<int32_t>(tm);
+    e.tile_base = total;
+    total += tm * tn;
+    min_tiles = std::min(min_tiles, tm * tn);
+    if (total > kMaxTiles) return ADA_ESHAPE;
+  }
+  ada::MergeEntry& sentinel = ent[n_proj];
+  sentinel = ada::MergeEntry{};
+  sentinel.tile_base = total;
+
+  // bucket size 2^shift <= smallest entry, so a bucket overlaps at most two entries
+  int32_t shift = 0;
+  while ((int64_t(2) << shift) <= min_tiles && shift < 30) ++shift;
+  const int64_t n_buckets = ((total - 1) >> shift) + 1;
+  std::vector<int32_t> lut(static_cast<size_t>(n_buckets));
+  for (int32_t i = 0, b = 0; b < n_buckets; ++b) {
+    const int64_t t = int64_t(b) << shift;
+    while (t >= ent[i + 1].tile_base) ++i;
+    lut[b] = i;
+  }
+
+  const size_t ent_bytes = ent.size() * sizeof(ada::MergeEntry);
+  const size_t bytes = ent_bytes + lut.size() * sizeof(int32_t);
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return ADA_EHIP;
+  void* dev = nullptr;
+  if (hipMalloc(&dev, bytes) != hipSuccess) return ADA_ENOMEM;
+  std::vector<unsigned char> host(bytes);
+  std::copy_n(reinterpret_cast<const unsigned char*>(ent.data()), ent_bytes, host.data());
+  std::copy_n(reinterpret_cast<const unsigned char*>(lut.data()), lut.size() * sizeof(int32_t),
+              host.data() + ent_bytes);
+  if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dev);
+    return ADA_EHIP;
+  }
+  ada_model_s* m = new (std::nothrow) ada_model_s{};
+  if (m == nullptr) {
+    (void)hipFree(dev);
+    return ADA_ENOMEM;
+  }
+  m->magic = kModelMagic;
+  m->dtype = dtype;
+  m->E = E;
+  m->r = r;
+  m->n_proj = n_proj;
+  m->lut_shift = shift;
+  m->device = device;
+  m->total_tiles = total;
+  m->dev = dev;
+  m->entries = static_cast<const ada::MergeEntry*>(dev);
+  m->lut = reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(dev) + ent_bytes);
+  *out = m;
+  return ADA_OK;
+}
+
+void ada_model_destroy(ada_model m) {
+  if (!model_ok(m)) return;
+  m->magic = 0;
+  (void)hipFree(m->dev);
+  delete m;
+}
+
+int64_t ada_model_tiles(ada_model m) {
+  if (!model_ok(m)) return ADA_EINVAL;
+  return m->total_tiles;
+}
+
+int ada_pregate(const void* h, const void* router, int32_t d, int32_t E, int32_t k, int32_t dtype,
+                int32_t renorm, int32_t* idx_out, float* gate_out, void* stream) {
+  if (h == nullptr || router == nullptr || idx_out == nullptr || gate_out == nullptr) return ADA_EINVAL;
+  if (!dtype_ok(dtype)) return ADA_EDTYPE;
+  if (renorm != 0 && renorm != 1) return ADA_EINVAL;
+  if (!aligned16(h) || !aligned16(router) || !aligned4(idx_out) || !aligned4(gate_out)) return ADA_EALIGN;
+  if (!dim_ok(d) || E < 1 || E > 64 || k < 1 || k > E) return ADA_ESHAPE;
+  const hipError_t e = ada::launch_pregate(h, router, d, E, k, dtype, renorm, idx_out, gate_out,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : ADA_EHIP;
+}
+
+int ada_merge(ada_model m, const int32_t* idx, const float* gate, int32_t k, float scale,
+              void* stream) {
+  if (!model_ok(m)) return ADA_EINVAL;
+  if (int s = check_selection(m, idx, gate, k); s != ADA_OK) return s;
+  if (int64_t(k) * m->r > ada::kMaxKR) return ADA_ESHAPE;
+  const ada::Selection s0{idx, gate, k, scale};
+  const ada::Selection s1{nullptr, nullptr, 0, 0.f};
+  return launch_merge_common(m, s0, s1, 0, k * m->r, stream);
+}
+
+int ada_unmerge(ada_model m, const int32_t* idx, const float* gate, int32_t k, float scale,
+                void* stream) {
+  if (!model_ok(m)) return ADA_EINVAL;
+  if (int s = check_selection(m, idx, gate, k); s != ADA_OK) return s;
+  if (int64_t(k) * m->r > ada::kMaxKR) return ADA_ESHAPE;
+  const ada::Selection s0{idx, gate, k, -scale};
+  const ada::Selection s1{nullptr, nullptr, 0, 0.f};
+  return launch_merge_common(m, s0, s1, 1, k * m->r, stream);
+}
+
+int ada_switch(ada_model m, const int32_t* idx_prev, const float* gate_prev, int32_t k_prev,
+               const int32_t* idx_cur, const float* gate_cur, int32_t k_cur, float scale,
+               void* stream) {
+  if (!model_ok(m)) return ADA_EINVAL;
+  if (int s = check_selection(m, idx_prev, gate_prev, k_prev); s != ADA_OK) return s;
+  if (int s = check_selection(m, idx_cur, gate_cur, k_cur); s != ADA_OK) return s;
+  if (int64_t(k_prev + k_cur) * m->r > ada::kMaxKR) return ADA_ESHAPE;
+  const ada::Selection s0{idx_prev, gate_prev, k_prev, -scale};
+  const ada::Selection s1{idx_cur, gate_cur, k_cur, scale};
+  return launch_merge_common(m, s0, s1, 1, (k_prev + k_cur) * m->r, stream);
+}
+
+int ada_decode_gemv(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w, const void* x,
+                    void* y, int32_t dtype, void* stream) {
+  if (w == nullptr || x == nullptr || y == nullptr) return ADA_EINVAL;
+  if (!dtype_ok(dtype)) return ADA_EDTYPE;
+  if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return ADA_EALIGN;
+  if (!dim_ok(d_out) || !dim_ok(d_in) || ld_w < d_in || ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
+  if ((ld_w * (dtype == ADA_BF16 ? 2 : 4)) % 16 != 0) return ADA_EALIGN;
+  const hipError_t e = ada::launch_gemv(w, d_out, d_in, ld_w, x, y, nullptr, dtype,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : ADA_EHIP;
+}
+
+int ada_lora_apply(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w, const void* a,
+                   const void* b, int32_t E, int32_t r, const int32_t* idx, const float* gate,
+                   int32_t k, float scale, const void* x, void* y, void* workspace,
+                   int64_t workspace_bytes, int32_t dtype, void* stream) {
+  if (w == nullptr || a == nullptr || b == nullptr || idx == nullptr || gate == nullptr ||
+      x == nullptr || y == nullptr || workspace == nullptr)
+    return ADA_EINVAL;
+  if (!dtype_ok(dtype)) return ADA_EDTYPE;
+  if (!aligned16(w) || !aligned16(a) || !aligned16(b) || !aligned16(x) || !aligned16(y) ||
+      !aligned16(workspace) || !aligned4(idx) || !aligned4(gate))
+    return ADA_EALIGN;
+  if (!dim_ok(d_out) || !dim_ok(d_in) || ld_w < d_in || ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
+  if ((ld_w * (dtype == ADA_BF16 ? 2 : 4)) % 16 != 0) return ADA_EALIGN;
+  if (E < 1 || E > 64 || r < 1 || k < 1 || k > E || int64_t(k) * r > ada::kMaxKR) return ADA_ESHAPE;
+  if (workspace_bytes < (int64_t(d_out) + int64_t(k) * r) * 4) return ADA_ESHAPE;
+  float* y32 = static_cast<float*>(workspace);
+  float* t = y32 + d_out;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ada::launch_gemv(w, d_out, d_in, ld_w, x, nullptr, y32, dtype, s) != hipSuccess) return ADA_EHIP;
+  if (ada::launch_lora_shrink(a, E, r, d_in, idx, k, x, t, dtype, s) != hipSuccess) return ADA_EHIP;
+  if (ada::launch_lora_expand(b, E, r, d_out, idx, gate, k, scale, y32, t, y, dtype, s) != hipSuccess)
+    return ADA_EHIP;
+  return ADA_OK;
+}
+
+}  // extern "C"

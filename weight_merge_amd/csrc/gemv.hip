@@ -1,0 +1,182 @@
+// Decode-step GEMV on the merged backbone, and the kernels of the unmerged,
+// per-layer routed baseline.
+//
+// "AdaFuse: Accelerating Dynamic Adapter Inference via Token-Level Pre-Gating and
+// Fused Kernel Optimization", Portuguese summary page, technical summary 2.B:
+// after the adapters are fused into the backbone, decoding runs with no routing,
+// so each projection of a batch-1 decode step is y = W' x.  That product reads
+// every weight once and does 2 flops per weight: bound by HBM bandwidth.
+//
+// The baseline (technical summary 1 on both pages: conventional dynamic adapters
+// route and apply adapters per layer, with several kernel calls per layer) keeps
+// the adapters separate: base GEMV (fp32 out), shrink t = A_sel x, expand
+// y = RNE(y32 + s * sum_j g_j B_j t_j).
+#include "common.h"
+
+namespace ada {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ void dot8(uint4 a, uint4 b, float& acc, uint16_t) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), acc);
+    acc = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(bv[i] & 0xffff0000u), acc);
+  }
+}
+
+__device__ __forceinline__ void dot8(uint4 a, uint4 b, float& acc, float) {
+  acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+  acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+  acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+  acc = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  f32x2 v = {f, 0.f};
+  return uint16_t(__builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t)) & 0xffffu);
+}
+
+__device__ __forceinline__ void store_out(uint16_t* y, int i, float v) { y[i] = to_bf16(v); }
+__device__ __forceinline__ void store_out(float* y, int i, float v) { y[i] = v; }
+
+__device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) {
+  return __uint_as_float(uint32_t(p[i]) << 16);
+}
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
+
+// Each wave owns ROWS consecutive rows and walks them with 16-byte loads, lanes
+// striding over the row; one butterfly per row at the end.
+template <typename T, int ROWS>
+__global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ W, int d_out, int d_in,
+                                                   int64_t ld, const T* __restrict__ x,
+                                                   T* __restrict__ y, float* __restrict__ y32) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
+  if (row0 >= d_out) return;
+  const int nvec = d_in / VEC;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const uint4* wr[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int row = row0 + r < d_out ? row0 + r : d_out - 1;  // clamp: duplicate rows are discarded
+    wr[r] = reinterpret_cast<const uint4*>(W + int64_t(row) * ld);
+  }
+  float acc[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) acc[r] = 0.f;
+#pragma unroll 4
+  for (int v = lane; v < nvec; v += 64) {
+    const uint4 xx = xv[v];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) dot8(wr[r][v], xx, acc[r], T());
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const float s = wave_sum(acc[r]);
+    if (lane == 0 && row0 + r < d_out) {
+      if (y32)
+        y32[row0 + r] = s;
+      else
+        store_out(y, row0 + r, s);
+    }
+  }
+}
+
+// t[j*r + rr] = A[idx_j][rr] . x for every slot j < k (0 for an out-of-range index).
+template <typename T>
+__global__ void __launch_bounds__(256) lora_shrink_kernel(const T* __restrict__ A, int E, int r,
+                                                          int d_in, const int32_t* __restrict__ idx,
+                                                          int k, const T* __restrict__ x,
+                                                          float* __restrict__ t) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= k * r) return;
+  const int j = row / r, rr = row - j * r;
+  const int e = idx[j];
+  float acc = 0.f;
+  if (e >= 0 && e < E) {
+    const uint4* ar = reinterpret_cast<const uint4*>(A + (int64_t(e) * r + rr) * d_in);
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    const int nvec = d_in / VEC;
+    for (int v = lane; v < nvec; v += 64) dot8(ar[v], xv[v], acc, T());
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) t[row] = acc;
+}
+
+// y[i] = RNE(y32[i] + sum_j scale * gate[j] * sum_rr B[idx_j][i][rr] t[j*r + rr]).
+template <typename T>
+__global__ void __launch_bounds__(256) lora_expand_kernel(const T* __restrict__ B, int E, int r,
+                                                          int d_out, const int32_t* __restrict__ idx,
+                                                          const float* __restrict__ gate, int k,
+                                                          float scale, const float* __restrict__ y32,
+                                                          const float* __restrict__ t,
+                                                          T* __restrict__ y) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d_out) return;
+  float acc = y32[i];
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[j];
+    const float c = scale * gate[j];
+    if (e < 0 || e >= E || c == 0.f) continue;
+    const T* br = B + (int64_t(e) * d_out + i) * r;
+    float s = 0.f;
+    for (int rr = 0; rr < r; ++rr) s = fmaf(load_elem(br, rr), t[j * r + rr], s);
+    acc = fmaf(c, s, acc);
+  }
+  store_out(y, i, acc);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const void* w, int d_out, int d_in, int64_t ld, const void* x, void* y,
+                       float* y32, int dtype, hipStream_t s) {
+  constexpr int ROWS = 2;
+  const dim3 grid((d_out + 4 * ROWS - 1) / (4 * ROWS)), block(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL((gemv_kernel<uint16_t, ROWS>), grid, block, 0, s, static_cast<const uint16_t*>(w),
+                       d_out, d_in, ld, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), y32);
+  else
+    hipLaunchKernelGGL((gemv_kernel<float, ROWS>), grid, block, 0, s, static_cast<const float*>(w), d_out,
+                       d_in, ld, static_cast<const float*>(x), static_cast<float*>(y), y32);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_shrink(const void* a, int E, int r, int d_in, const int32_t* idx, int k,
+                              const void* x, float* t, int dtype, hipStream_t s) {
+  const dim3 grid((k * r + 3) / 4), block(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(lora_shrink_kernel<uint16_t>, grid, block, 0, s, static_cast<const uint16_t*>(a),
+                       E, r, d_in, idx, k, static_cast<const uint16_t*>(x), t);
+  else
+    hipLaunchKernelGGL(lora_shrink_kernel<float>, grid, block, 0, s, static_cast<const float*>(a), E, r,
+                       d_in, idx, k, static_cast<const float*>(x), t);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_expand(const void* b, int E, int r, int d_out, const int32_t* idx,
+                              const float* gate, int k, float scale, const float* y32,
+                              const float* t, void* y, int dtype, hipStream_t s) {
+  const dim3 grid((d_out + 255) / 256), block(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(lora_expand_kernel<uint16_t>, grid, block, 0, s, static_cast<const uint16_t*>(b),
+                       E, r, d_out, idx, gate, k, scale, y32, t, static_cast<uint16_t*>(y));
+  else
+    hipLaunchKernelGGL(lora_expand_kernel<float>, grid, block, 0, s, static_cast<const float*>(b), E, r,
+                       d_out, idx, gate, k, scale, y32, t, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+}  // namespace ada
