@@ -92,7 +92,8 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
   if (!dtype_ok(dtype)) return ADA_EDTYPE;
   if (n_proj < 1 || n_proj > (1 << 20)) return ADA_ESHAPE;
   if (E < 1 || E > 64 || r < 1 || r > ada::kMaxKR) return ADA_ESHAPE;
-  const int tile = dtype == ADA_BF16 ? ada::kTileBF16 : ada::kTileF32;
+  const int tile_r = dtype == ADA_BF16 ? ada::kTileBF16Rows : ada::kTileF32;
+  const int tile_c = dtype == ADA_BF16 ? ada::kTileBF16Cols : ada::kTileF32;
   const int esz = dtype == ADA_BF16 ? 2 : 4;
 
   std::vector<ada::MergeEntry> ent(static_cast<size_t>(n_proj) + 1);
@@ -106,7 +107,7 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
     if (!dim_ok(p.d_out) || !dim_ok(p.d_in)) return ADA_ESHAPE;
     if (p.ld_w < p.d_in || p.ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
     if ((p.ld_w * esz) % 16 != 0) return ADA_EALIGN;
-    const int64_t tm = (p.d_out + tile - 1) / tile, tn = (p.d_in + tile - 1) / tile;
+    const int64_t tm = (p.d_out + tile_r - 1) / tile_r, tn = (p.d_in + tile_c - 1) / tile_c;
     ada::MergeEntry& e = ent[i];
     e.w = p.w;
     e.w_out = p.w_out != nullptr ? p.w_out : p.w;
@@ -201,7 +202,7 @@ int ada_merge(ada_model m, const int32_t* idx, const float* gate, int32_t k, flo
   if (int s = check_selection(m, idx, gate, k); s != ADA_OK) return s;
   if (int64_t(k) * m->r > ada::kMaxKR) return ADA_ESHAPE;
   const ada::Selection s0{idx, gate, k, scale};
-  const ada::Selection s1{nullptr, nullptr, 0, 0.f};
+  const ada::Selection s1{idx, gate, 0, 0.f};  // empty; pointers valid for branch-free reads
   return launch_merge_common(m, s0, s1, 0, k * m->r, stream);
 }
 
@@ -211,7 +212,7 @@ int ada_unmerge(ada_model m, const int32_t* idx, const float* gate, int32_t k, f
   if (int s = check_selection(m, idx, gate, k); s != ADA_OK) return s;
   if (int64_t(k) * m->r > ada::kMaxKR) return ADA_ESHAPE;
   const ada::Selection s0{idx, gate, k, -scale};
-  const ada::Selection s1{nullptr, nullptr, 0, 0.f};
+  const ada::Selection s1{idx, gate, 0, 0.f};  // empty; pointers valid for branch-free reads
   return launch_merge_common(m, s0, s1, 1, k * m->r, stream);
 }
 

@@ -7,7 +7,15 @@
 namespace ada {
 
 // Output tile of one merge workgroup.
-constexpr int kTileBF16 = 128;  // 128 x 128 for bf16 storage (MFMA path)
+#ifndef ADA_BF16_ROW_BLOCKS
+#define ADA_BF16_ROW_BLOCKS 2
+#endif
+#ifndef ADA_NT_STORE
+#define ADA_NT_STORE 0
+#endif
+constexpr int kBF16RowBlocks = ADA_BF16_ROW_BLOCKS;  // 16-row MFMA blocks per wave
+constexpr int kTileBF16Rows = 32 * kBF16RowBlocks;   // bf16 tile: kTileBF16Rows x kTileBF16Cols
+constexpr int kTileBF16Cols = 128;
 constexpr int kTileF32 = 64;    // 64 x 64 for fp32 storage (VALU path)
 constexpr int kMaxSlots = 128;  // selected adapters per launch (two selections of <= 64)
 constexpr int kMaxKR = 512;     // k * r bound of one launch
