@@ -78,6 +78,12 @@ MERGE_CASES = [
     (1, 16, 1, 8, 8, "bf16", True),
     (16, 128, 4, 264, 1032, "bf16", True),
     (3, 1, 3, 24, 16, "bf16", False),
+    # every (tile, rank mode) kernel: r a multiple of 8 but not a power of two, and
+    # r not a multiple of 8, on both the 64-row and the 128-row tiles
+    (4, 24, 2, 136, 264, "bf16", True),
+    (6, 40, 3, 264, 392, "bf16", False),
+    (8, 12, 8, 136, 264, "bf16", True),
+    (8, 16, 4, 200, 136, "bf16", False),
 ]
 
 

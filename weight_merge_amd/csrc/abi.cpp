@@ -17,6 +17,7 @@ namespace {
 constexpr uint64_t kModelMagic = 0x6164614675736521ull;
 constexpr int64_t kMaxDim = int64_t(1) << 22;     // rows or columns of one projection
 constexpr int64_t kMaxTiles = (int64_t(1) << 24) - 1;  // one grid: tiles * 256 threads < 2^32
+constexpr int64_t kMaxElems = int64_t(1) << 31;        // per W matrix and per adapter bank
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -25,18 +26,25 @@ bool dtype_ok(int32_t dt) { return dt == ADA_F32 || dt == ADA_BF16; }
 
 }  // namespace
 
+// One tile decomposition of the registered projections: the work table (one entry
+// per projection plus a sentinel) and the tile -> entry lookup buckets.
+struct TileTable {
+  const ada::MergeEntry* entries;
+  const int32_t* lut;
+  int64_t total_tiles;
+  int32_t lut_shift;
+  int32_t tile_rows;
+};
+
 struct ada_model_s {
   uint64_t magic;
   int32_t dtype;
   int32_t E;
   int32_t r;
   int32_t n_proj;
-  int32_t lut_shift;
   int32_t device;
-  int64_t total_tiles;
-  void* dev;                      // one allocation: entries, then the lookup table
-  const ada::MergeEntry* entries;
-  const int32_t* lut;
+  void* dev;          // one allocation holding both tables
+  TileTable tab[2];   // bf16: [0] 64-row tiles (k*r <= 64), [1] 128-row tiles; fp32: both 64 x 64
 };
 
 namespace {
@@ -45,21 +53,70 @@ bool model_ok(const ada_model_s* m) { return m != nullptr && m->magic == kModelM
 
 int launch_merge_common(ada_model m, const ada::Selection& s0, const ada::Selection& s1,
                         int src_is_out, int kr_max, void* stream) {
+  const TileTable& t = m->tab[m->dtype == ADA_BF16 && kr_max > ada::kLongKR ? 1 : 0];
   ada::MergeParams p{};
-  p.table = m->entries;
-  p.lut = m->lut;
-  p.total_tiles = m->total_tiles;
-  p.lut_shift = m->lut_shift;
+  p.table = t.entries;
+  p.lut = t.lut;
+  p.total_tiles = t.total_tiles;
+  p.lut_shift = t.lut_shift;
   p.n_entries = m->n_proj;
   p.sel[0] = s0;
   p.sel[1] = s1;
   p.E = m->E;
   p.r = m->r;
+  p.r_shift = (m->r & (m->r - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(m->r)) : -1;
   p.src_is_out = src_is_out;
   p.xcd_remap = 1;
   const hipError_t e = ada::launch_merge(p, m->dtype, kr_max, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADA_OK : ADA_EHIP;
 }
+
+// Host image of one tile decomposition.
+struct HostTable {
+  std::vector<ada::MergeEntry> ent;
+  std::vector<int32_t> lut;
+  int64_t total = 0;
+  int32_t shift = 0;
+  int32_t tile_rows = 0;
+};
+
+int build_table(const ada_proj* projs, int32_t n_proj, int tile_r, int tile_c, HostTable& h) {
+  h.tile_rows = tile_r;
+  h.ent.assign(static_cast<size_t>(n_proj) + 1, ada::MergeEntry{});
+  int64_t min_tiles = INT64_MAX;
+  for (int32_t i = 0; i < n_proj; ++i) {
+    const ada_proj& p = projs[i];
+    const int64_t tm = (p.d_out + tile_r - 1) / tile_r, tn = (p.d_in + tile_c - 1) / tile_c;
+    ada::MergeEntry& e = h.ent[i];
+    e.w = p.w;
+    e.w_out = p.w_out != nullptr ? p.w_out : p.w;
+    e.a = p.a;
+    e.b = p.b;
+    e.ld = p.ld_w;
+    e.d_out = p.d_out;
+    e.d_in = p.d_in;
+    e.tiles_n = static_cast<int32_t>(tn);
+    e.tiles_m = static_cast<int32_t>(tm);
+    e.tile_base = h.total;
+    h.total += tm * tn;
+    min_tiles = std::min(min_tiles, tm * tn);
+    if (h.total > kMaxTiles) return ADA_ESHAPE;
+  }
+  h.ent[n_proj].tile_base = h.total;  // sentinel
+  // bucket size 2^shift <= smallest entry, so a bucket overlaps at most two entries
+  while ((int64_t(2) << h.shift) <= min_tiles && h.shift < 30) ++h.shift;
+  const int64_t n_buckets = ((h.total - 1) >> h.shift) + 1;
+  h.lut.resize(static_cast<size_t>(n_buckets));
+  int32_t i = 0;
+  for (int64_t b = 0; b < n_buckets; ++b) {
+    const int64_t t = b << h.shift;
+    while (t >= h.ent[i + 1].tile_base) ++i;
+    h.lut[b] = i;
+  }
+  return ADA_OK;
+}
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
 int check_selection(const ada_model_s* m, const int32_t* idx, const float* gate, int32_t k) {
   if (idx == nullptr || gate == nullptr) return ADA_EINVAL;
@@ -92,12 +149,7 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
   if (!dtype_ok(dtype)) return ADA_EDTYPE;
   if (n_proj < 1 || n_proj > (1 << 20)) return ADA_ESHAPE;
   if (E < 1 || E > 64 || r < 1 || r > ada::kMaxKR) return ADA_ESHAPE;
-  const int tile_r = dtype == ADA_BF16 ? ada::kTileBF16Rows : ada::kTileF32;
-  const int tile_c = dtype == ADA_BF16 ? ada::kTileBF16Cols : ada::kTileF32;
   const int esz = dtype == ADA_BF16 ? 2 : 4;
-
-  std::vector<ada::MergeEntry> ent(static_cast<size_t>(n_proj) + 1);
-  int64_t total = 0, min_tiles = INT64_MAX;
   for (int32_t i = 0; i < n_proj; ++i) {
     const ada_proj& p = projs[i];
     if (p.w == nullptr || p.a == nullptr || p.b == nullptr) return ADA_EINVAL;
@@ -107,47 +159,37 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
     if (!dim_ok(p.d_out) || !dim_ok(p.d_in)) return ADA_ESHAPE;
     if (p.ld_w < p.d_in || p.ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
     if ((p.ld_w * esz) % 16 != 0) return ADA_EALIGN;
-    const int64_t tm = (p.d_out + tile_r - 1) / tile_r, tn = (p.d_in + tile_c - 1) / tile_c;
-    ada::MergeEntry& e = ent[i];
-    e.w = p.w;
-    e.w_out = p.w_out != nullptr ? p.w_out : p.w;
-    e.a = p.a;
-    e.b = p.b;
-    e.ld = p.ld_w;
-    e.d_out = p.d_out;
-    e.d_in = p.d_in;
-    e.tiles_n = static_cast<int32_t>(tn);
-    e.tiles_m = static_cast<int32_t>(tm);
-    e.tile_base = total;
-    total += tm * tn;
-    min_tiles = std::min(min_tiles, tm * tn);
-    if (total > kMaxTiles) return ADA_ESHAPE;
+    // the merge kernels address W and the adapter banks with 32-bit element offsets
+    if (int64_t(p.d_out) * p.ld_w >= kMaxElems || int64_t(E) * r * p.d_in >= kMaxElems ||
+        int64_t(E) * r * p.d_out >= kMaxElems)
+      return ADA_ESHAPE;
   }
-  ada::MergeEntry& sentinel = ent[n_proj];
-  sentinel = ada::MergeEntry{};
-  sentinel.tile_base = total;
-
-  // bucket size 2^shift <= smallest entry, so a bucket overlaps at most two entries
-  int32_t shift = 0;
-  while ((int64_t(2) << shift) <= min_tiles && shift < 30) ++shift;
-  const int64_t n_buckets = ((total - 1) >> shift) + 1;
-  std::vector<int32_t> lut(static_cast<size_t>(n_buckets));
-  for (int32_t i = 0, b = 0; b < n_buckets; ++b) {
-    const int64_t t = int64_t(b) << shift;
-    while (t >= ent[i + 1].tile_base) ++i;
-    lut[b] = i;
+  HostTable ht[2];
+  for (int t = 0; t < 2; ++t) {
+    const int kr = t == 0 ? ada::kLongKR : ada::kMaxKR;
+    const int tile_r = dtype == ADA_BF16 ? ada::bf16_tile_rows(kr) : ada::kTileF32;
+    const int tile_c = dtype == ADA_BF16 ? ada::bf16_tile_cols(kr) : ada::kTileF32;
+    if (int st = build_table(projs, n_proj, tile_r, tile_c, ht[t]); st != ADA_OK) return st;
   }
 
-  const size_t ent_bytes = ent.size() * sizeof(ada::MergeEntry);
-  const size_t bytes = ent_bytes + lut.size() * sizeof(int32_t);
+  size_t off[4], bytes = 0;
+  for (int t = 0; t < 2; ++t) {
+    off[2 * t] = bytes;
+    bytes = align16(bytes + ht[t].ent.size() * sizeof(ada::MergeEntry));
+    off[2 * t + 1] = bytes;
+    bytes = align16(bytes + ht[t].lut.size() * sizeof(int32_t));
+  }
+  std::vector<unsigned char> host(bytes, 0);
+  for (int t = 0; t < 2; ++t) {
+    std::copy_n(reinterpret_cast<const unsigned char*>(ht[t].ent.data()),
+                ht[t].ent.size() * sizeof(ada::MergeEntry), host.data() + off[2 * t]);
+    std::copy_n(reinterpret_cast<const unsigned char*>(ht[t].lut.data()), ht[t].lut.size() * sizeof(int32_t),
+                host.data() + off[2 * t + 1]);
+  }
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return ADA_EHIP;
   void* dev = nullptr;
   if (hipMalloc(&dev, bytes) != hipSuccess) return ADA_ENOMEM;
-  std::vector<unsigned char> host(bytes);
-  std::copy_n(reinterpret_cast<const unsigned char*>(ent.data()), ent_bytes, host.data());
-  std::copy_n(reinterpret_cast<const unsigned char*>(lut.data()), lut.size() * sizeof(int32_t),
-              host.data() + ent_bytes);
   if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(dev);
     return ADA_EHIP;
@@ -162,12 +204,16 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
   m->E = E;
   m->r = r;
   m->n_proj = n_proj;
-  m->lut_shift = shift;
   m->device = device;
-  m->total_tiles = total;
   m->dev = dev;
-  m->entries = static_cast<const ada::MergeEntry*>(dev);
-  m->lut = reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(dev) + ent_bytes);
+  for (int t = 0; t < 2; ++t) {
+    unsigned char* base = static_cast<unsigned char*>(dev);
+    m->tab[t].entries = reinterpret_cast<const ada::MergeEntry*>(base + off[2 * t]);
+    m->tab[t].lut = reinterpret_cast<const int32_t*>(base + off[2 * t + 1]);
+    m->tab[t].total_tiles = ht[t].total;
+    m->tab[t].lut_shift = ht[t].shift;
+    m->tab[t].tile_rows = ht[t].tile_rows;
+  }
   *out = m;
   return ADA_OK;
 }
@@ -181,7 +227,7 @@ void ada_model_destroy(ada_model m) {
 
 int64_t ada_model_tiles(ada_model m) {
   if (!model_ok(m)) return ADA_EINVAL;
-  return m->total_tiles;
+  return m->tab[0].total_tiles;
 }
 
 int ada_pregate(const void* h, const void* router, int32_t d, int32_t E, int32_t k, int32_t dtype,

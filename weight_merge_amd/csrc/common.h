@@ -6,16 +6,29 @@
 
 namespace ada {
 
-// Output tile of one merge workgroup.
-#ifndef ADA_BF16_ROW_BLOCKS
-#define ADA_BF16_ROW_BLOCKS 2
+// Output tile of one merge workgroup (bf16).  A tile shape is RB row blocks and CT
+// column blocks of 16 per wave, with the 4 waves arranged (4 / WGN) x WGN; short
+// contractions (k*r <= kLongKR) and long ones use separate shapes.
+#ifndef ADA_SHORT_TILE
+#define ADA_SHORT_TILE 2, 4, 2
 #endif
-#ifndef ADA_NT_STORE
-#define ADA_NT_STORE 0
+#ifndef ADA_LONG_TILE
+#define ADA_LONG_TILE 4, 4, 2
 #endif
-constexpr int kBF16RowBlocks = ADA_BF16_ROW_BLOCKS;  // 16-row MFMA blocks per wave
-constexpr int kTileBF16Rows = 32 * kBF16RowBlocks;   // bf16 tile: kTileBF16Rows x kTileBF16Cols
-constexpr int kTileBF16Cols = 128;
+template <int RB, int CT, int WGN>
+struct TileShapeT {
+  static constexpr int rb = RB, ct = CT, wgn = WGN;
+  static constexpr int rows = 16 * RB * (4 / WGN), cols = 16 * CT * WGN;
+};
+using ShortTile = TileShapeT<ADA_SHORT_TILE>;
+using LongTile = TileShapeT<ADA_LONG_TILE>;
+constexpr int kLongKR = 64;
+__host__ __device__ constexpr int bf16_tile_rows(int kr_max) {
+  return kr_max <= kLongKR ? ShortTile::rows : LongTile::rows;
+}
+__host__ __device__ constexpr int bf16_tile_cols(int kr_max) {
+  return kr_max <= kLongKR ? ShortTile::cols : LongTile::cols;
+}
 constexpr int kTileF32 = 64;    // 64 x 64 for fp32 storage (VALU path)
 constexpr int kMaxSlots = 128;  // selected adapters per launch (two selections of <= 64)
 constexpr int kMaxKR = 512;     // k * r bound of one launch
@@ -53,6 +66,7 @@ struct MergeParams {
   Selection sel[2];
   int32_t E;
   int32_t r;
+  int32_t r_shift;     // log2(r) when r is a power of two, else -1
   int32_t src_is_out;  // 1: read the merged buffer (w_out) instead of w
   int32_t xcd_remap;   // 1: give each XCD a contiguous range of tiles
 };

@@ -9,25 +9,27 @@
 //                                      A_cat = [A_{e_1}; ...; A_{e_k}],
 // with c_j = +scale * g_j to fuse and -scale * g_j to de-fuse.  The pages split the
 // product into GEMM tiles per thread block and hide global-memory latency with a
-// prefetch buffer; here one workgroup owns one 64 x 128 output tile of one
-// projection, found through a work table, so a single grid covers all layers.
+// prefetch buffer; here one workgroup owns one 64 x 128 (or 128 x 128) output tile of
+// one projection, found through a work table, so a single grid covers all layers.
 //
 // The merge is bound by HBM: every weight is read once and written once, while
 // the rank-(k*r) product costs 2*k*r flops per weight.  The layout choices serve
 // that stream:
-//   * W goes from HBM straight to registers and back, never through LDS.  The
-//     MFMA's M index is mapped to W columns and its N index to W rows, so each
-//     lane's four accumulator values are four adjacent columns of one row; with
-//     a column permutation inside each 64-column strip every lane owns two runs of
-//     8 adjacent columns, loaded and stored as 16-byte vectors.
-//   * A_cat and B_cat for the tile are gathered into LDS once per K chunk, with the
-//     gate and scale folded into B_cat (rounded to bf16), A_cat stored transposed so
-//     every MFMA operand fragment is one 16-byte LDS read.
+//   * W goes from HBM to registers and back in a row-major pattern: each load or
+//     store instruction covers whole 256-byte row segments of the tile.  The MFMA's
+//     M index is mapped to W columns and its N index to W rows, so each lane's four
+//     accumulator values are four adjacent columns of one row; the accumulators
+//     reach the W layout through one fp32 pass in LDS.
+//   * A_cat and B_cat for the tile are gathered into LDS once per K chunk (double
+//     buffered), with the gate and scale folded into B_cat (rounded to bf16).  Both
+//     are stored as they lie in memory (16-byte writes); the A operand's transpose
+//     happens in the LDS read (ds_read_b64_tr_b16).
 //   * The W loads are issued first, straight after the tile lookup, with every load
 //     on the path branch-free and in the global address space, so no wait for the
 //     selection or the adapter gathers also waits for the W tile.
-//   * Small tiles (64 x 128) keep registers low: four waves per SIMD, so many tiles'
-//     W loads are in flight on each CU.
+//   * Small tiles (64 x 128) keep registers low for short contractions: four waves
+//     per SIMD, so many tiles' W loads are in flight on each CU.  Long contractions
+//     (k*r > 64) use 128 x 128 tiles so each gathered adapter byte serves more weights.
 //   * Workgroup ids are remapped so each XCD walks a contiguous range of tiles,
 //     keeping a projection's adapter rows and columns in that XCD's L2.
 #include "common.h"
@@ -52,6 +54,8 @@ __device__ __forceinline__ ADA_GLOBAL T* as_global_mut(void* p) {
 }
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -141,26 +145,63 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 
 // ---------------------------------------------------------------- bf16, MFMA path
 //
-// Workgroup: 4 waves in a 2 x 2 arrangement, each owning a (16 RB) x 64 sub-tile made
-// of RB x 4 MFMA blocks of 16 x 16 (v_mfma_f32_16x16x32_bf16); the workgroup tile is
-// (32 RB) x 128.  For block (rb, ct) lane l = 16 q + i holds D[4q + c][i] =
-// delta[row 16 rb + i][col(ct, 4q + c)], with col(ct, m) = 32 (ct / 2) + 8 (m / 4) +
-// 4 (ct % 2) + m % 4 inside the wave's strip: lane (q, i) owns the columns
-// 32 h + 8 q + [0, 8) for h = 0, 1.
+// Workgroup: 4 waves arranged WGM x WGN (WGM = 4 / WGN); each wave owns a (16 RB) x
+// (16 CT) sub-tile made of RB x CT MFMA blocks of 16 x 16 (v_mfma_f32_16x16x32_bf16),
+// so the workgroup tile is (16 RB WGM) x (16 CT WGN).  MFMA index m runs over W
+// columns and n over W rows: for block (rb, ct), lane l = 16 q + i holds
+// D[4q + c][i] = delta[row 16 rb + i][col(ct, 4q + c)] with
+// col(ct, m) = 32 (ct / 2) + 8 (m / 4) + 4 (ct % 2) + m % 4 inside the wave's strip,
+// so lane (q, i) owns the columns 32 h + 8 q + [0, 8), h = 0 .. CT/2 - 1.
+//
+// Operands per K chunk of KC, double-buffered in LDS:
+//   Bs[row][k] = bf16(c_j * B_{e_j}[row][k - j r])   (rows of B_cat, gate folded in)
+//   As[k][col] = A_{e_j}[k - j r][col]               (rows of A_cat, as stored)
+// A B fragment (8 consecutive k of one row) is one 16-byte LDS read.  An A fragment
+// (8 consecutive k of one column) is gathered from the row-major As with two
+// ds_read_b64_tr_b16: inside each 16-lane group, lanes 4t..4t+3 point at 16 elements
+// of k row t (4 each, in column order col(ct, 4u .. 4u+3) for lane 4t+u) and lane c
+// receives element c of rows t = 0..3, i.e. 4 consecutive k of column col(ct, c).
 //
 // Order of work inside a workgroup, chosen so HBM never waits on the rest:
 //   1. wave 0 loads the selection (k indices and gates, L2-resident);
 //   2. every lane issues its W loads (the tile's HBM traffic);
 //   3. wave 0 compacts the active slots into LDS (waits for step 1 only);
-//   4. the adapter gathers for the first K chunk go to LDS; MFMAs run;
+//   4. K chunks: gather chunk c+1 into registers while the MFMAs consume chunk c;
 //   5. W + delta is rounded once and stored.
-template <int KC, int RB>
-__global__ void __launch_bounds__(256) merge_bf16_kernel(MergeParams p) {
-  constexpr int BM = 32 * RB, BN = 128;
-  constexpr int LDK = KC + 8;  // LDS row pitch in elements (16-byte pad)
-  static_assert((BM * KC / 8) % 256 == 0 && (KC * BN / 8) % 256 == 0, "staging split");
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t As[BN * LDK];
+//
+// RMODE fixes how the contraction index k maps to (slot j, rank rr) and how B is
+// gathered, so the K loop has no runtime branches:
+//   0: r a power of two and a multiple of 8 (shifts; 16-byte B vectors)
+//   1: r a multiple of 8 (division; 16-byte B vectors)
+//   2: any other r (division; B element by element)
+#ifndef ADA_WAVES_PER_EU
+#define ADA_WAVES_PER_EU 1
+#endif
+template <int KC, int RB, int CT, int WGN, int RMODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ADA_WAVES_PER_EU, 8)))
+merge_bf16_kernel(MergeParams p) {
+  constexpr int WGM = 4 / WGN;
+  constexpr int BM = 16 * RB * WGM, BN = 16 * CT * WGN;
+  constexpr int LDB = KC + 8;   // Bs row pitch (elements)
+  constexpr int LDA = BN + 8;   // As row pitch (elements)
+  constexpr int NBV = BM * KC / 8;  // 16-byte B vectors per chunk
+  constexpr int NAV = KC * BN / 8;  // 16-byte A vectors per chunk
+  constexpr int B_VPT = (NBV + 255) / 256;
+  constexpr int A_VPT = (NAV + 255) / 256;
+  static_assert(WGM * WGN == 4 && CT % 2 == 0 && NBV % 64 == 0 && NAV % 64 == 0, "tile shape");
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+  // LDS: the double-buffered operand chunks, and (after the last MFMA) the fp32 delta
+  // tile in the same bytes
+  constexpr int LDD = BN + 4;  // delta row pitch (floats): 16 rows of a 16-byte column write hit 64 banks
+  constexpr int STAGE_BYTES = 2 * (BM * LDB + KC * LDA) * 2;
+  constexpr int DELTA_BYTES = BM * LDD * 4;
+  constexpr int SMEM = STAGE_BYTES > DELTA_BYTES ? STAGE_BYTES : DELTA_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  uint16_t (*Bs)[BM * LDB] = reinterpret_cast<uint16_t (*)[BM * LDB]>(smem);
+  uint16_t (*As)[KC * LDA] = reinterpret_cast<uint16_t (*)[KC * LDA]>(smem + 2 * BM * LDB * 2);
+  float* Ds = reinterpret_cast<float*>(smem);
   __shared__ int s_exp[kMaxSlots];
   __shared__ float s_coef[kMaxSlots];
   __shared__ int s_n;
@@ -170,19 +211,18 @@ __global__ void __launch_bounds__(256) merge_bf16_kernel(MergeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4;
   const int li = lane & 15;
-  const int wy = wave >> 1, wx = wave & 1;
+  const int wy = wave / WGN, wx = wave % WGN;
 
   const TileRef T = find_tile(p, BM, BN);
-  static_assert(BM == kTileBF16Rows && BN == kTileBF16Cols, "tile matches the work table");
   const ADA_GLOBAL uint16_t* __restrict__ src = as_global<uint16_t>(T.src);
   ADA_GLOBAL uint16_t* __restrict__ dst = as_global_mut<uint16_t>(T.dst);
   const ADA_GLOBAL uint16_t* __restrict__ gA = as_global<uint16_t>(T.a);
   const ADA_GLOBAL uint16_t* __restrict__ gB = as_global<uint16_t>(T.b);
 
-  // 1. selection (wave 0): lane j holds slot j of each selection
-  // (branch-free: lanes past k re-read slot 0, which always exists, and are
-  // discarded below; exec-masked loads would make the compiler wait for every
-  // outstanding load, the W tile included, before the compaction)
+  // 1. selection (wave 0): lane j holds slot j of each selection (branch-free: lanes
+  // past k re-read slot 0, which always exists, and are discarded below; exec-masked
+  // loads would make the compiler wait for every outstanding load, the W tile
+  // included, before the compaction)
   int sel_e[2];
   float sel_g[2];
   if (wave == 0) {
@@ -194,20 +234,23 @@ __global__ void __launch_bounds__(256) merge_bf16_kernel(MergeParams p) {
     }
   }
 
-  // 2. this lane's W vectors: rows row0 + 16 RB wy + 16 rb + li, columns col0 + 64 wx + 32 h + 8 q
-  int64_t woff[RB][2];
-  bool ok[RB][2];
-  u32x4 wv[RB][2];
+  // 2. this thread's W vectors, row-major over the tile: vector v = tid + 256 u holds
+  //    row v / (BN/8), columns 8 (v % (BN/8)) .. + 7, so one load instruction covers
+  //    whole 256-byte row segments (the MFMA layout would give 16 rows x 64 bytes,
+  //    which streams about 20% slower)
+  constexpr int NV = BM * BN / 8 / 256;
+  static_assert(NV * 2048 == BM * BN, "W split");
+  uint32_t woff[NV];  // element offsets: every W matrix has fewer than 2^31 elements
+  bool ok[NV];
+  u32x4 wv[NV];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = T.row0 + 16 * RB * wy + 16 * rb + li;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int col = T.col0 + 64 * wx + 32 * h + 8 * q;
-      ok[rb][h] = row < T.d_out && col < T.d_in;
-      woff[rb][h] = ok[rb][h] ? int64_t(row) * T.ld + col : 0;  // out of range: re-read W[0][0..8)
-      wv[rb][h] = *reinterpret_cast<const ADA_GLOBAL u32x4*>(src + woff[rb][h]);
-    }
+  for (int u = 0; u < NV; ++u) {
+    const int v = tid + 256 * u;
+    const int row = T.row0 + v / (BN / 8);
+    const int col = T.col0 + 8 * (v % (BN / 8));
+    ok[u] = row < T.d_out && col < T.d_in;
+    woff[u] = ok[u] ? uint32_t(row) * uint32_t(T.ld) + uint32_t(col) : 0u;  // out of range: re-read W[0][0..8)
+    wv[u] = *reinterpret_cast<const ADA_GLOBAL u32x4*>(src + woff[u]);
   }
 
   // 3. active slots, in selection order: index in range and coefficient nonzero
@@ -234,20 +277,32 @@ __global__ void __launch_bounds__(256) merge_bf16_kernel(MergeParams p) {
     // Nothing selected: in place there is nothing to write; out of place, copy.
     if (T.src == T.dst) return;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (ok[rb][h]) *reinterpret_cast<ADA_GLOBAL u32x4*>(dst + woff[rb][h]) = wv[rb][h];
+    for (int u = 0; u < NV; ++u)
+      if (ok[u]) *reinterpret_cast<ADA_GLOBAL u32x4*>(dst + woff[u]) = wv[u];
     return;
   }
 
   const int r = p.r;
+  const int r_shift = p.r_shift;
   const int kr = nslot * r;
-  const bool rvec = (r & 7) == 0;
+  const int nchunks = (kr + KC - 1) / KC;
+  constexpr bool rvec = RMODE != 2;
+  // contraction index k -> (slot j, rank rr)
+  auto split = [&](int k, int& j, int& rr) {
+    if constexpr (RMODE == 0) {
+      j = k >> r_shift;
+      rr = k & (r - 1);
+    } else {
+      j = k / r;
+      rr = k - j * r;
+    }
+  };
 
-  // ---- K-chunk staging: global -> registers, then registers -> LDS.
-  constexpr int B_VPT = BM * KC / 8 / 256;  // 16-byte B vectors per thread
-  constexpr int A_VPT = KC * BN / 8 / 256;  // 16-byte A vectors per thread
+  // ---- K-chunk gathers: global -> registers (stage_load), registers -> LDS (stage_store).
+  // Branch-free: out-of-range slots, rows or columns re-read an in-range vector and are
+  // replaced by zeros.  Vector v of a chunk: B row v / (KC/8), k 8 (v % (KC/8));
+  // A k row v / (BN/8), columns 8 (v % (BN/8)).  Threads past the vector count (whole
+  // waves, as the counts are multiples of 64) skip.
   u32x4 sb[B_VPT];
   float sc[B_VPT];
   u32x4 sa[A_VPT];
@@ -256,31 +311,27 @@ __global__ void __launch_bounds__(256) merge_bf16_kernel(MergeParams p) {
 #pragma unroll
     for (int i = 0; i < B_VPT; ++i) {
       const int v = tid + 256 * i;
+      if (NBV % 256 != 0 && v >= NBV) break;
       const int row = v / (KC / 8);
       const int kv = v % (KC / 8);
       const int grow = T.row0 + row;
-      u32x4 val = (u32x4){0u, 0u, 0u, 0u};
-      float c = 0.f;
-      if (rvec) {
-        // branch-free gather: out-of-range slots/rows re-read an in-range vector and
-        // get a zero coefficient
-        const int k = k0 + 8 * kv;
-        const int j = k / r;
-        const int rr = k - j * r;
+      if constexpr (rvec) {
+        int j, rr;
+        split(k0 + 8 * kv, j, rr);
         const bool in = j < nslot && grow < T.d_out;
         const int js = in ? j : 0;
-        const int rs = in ? grow : 0;
-        val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(gB + (int64_t(s_exp[js]) * T.d_out + rs) * r + (in ? rr : 0));
-        c = in ? s_coef[js] : 0.f;
-        sc[i] = c;
+        const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(
+            gB + ((uint32_t(s_exp[js]) * uint32_t(T.d_out) + uint32_t(in ? grow : 0)) * uint32_t(r) +
+                  uint32_t(in ? rr : 0)));
+        sb[i] = in ? val : (u32x4){0u, 0u, 0u, 0u};
+        sc[i] = s_coef[js];
       } else {
-        // rank not a multiple of 8: gather element by element, coefficient applied here
+        // rank not a multiple of 8: element by element, coefficient applied here
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int k = k0 + 8 * kv + t;
-          const int j = k / r;
-          const int rr = k - j * r;
+          int j, rr;
+          split(k0 + 8 * kv + t, j, rr);
           float x = 0.f;
           if (j < nslot && grow < T.d_out)
             x = __uint_as_float(uint32_t(gB[(int64_t(s_exp[j]) * T.d_out + grow) * r + rr]) << 16) *
@@ -288,117 +339,130 @@ __global__ void __launch_bounds__(256) merge_bf16_kernel(MergeParams p) {
           const uint32_t hb = pack_bf16x2(x, 0.f) & 0xffffu;
           w[t >> 1] |= hb << (16 * (t & 1));
         }
-        val = (u32x4){w[0], w[1], w[2], w[3]};
+        sb[i] = (u32x4){w[0], w[1], w[2], w[3]};
         sc[i] = 1.f;
       }
-      sb[i] = val;
     }
 #pragma unroll
     for (int i = 0; i < A_VPT; ++i) {
       const int v = tid + 256 * i;
+      if (NAV % 256 != 0 && v >= NAV) break;
       const int kl = v / (BN / 8);
       const int cv = v % (BN / 8);
-      const int k = k0 + kl;
-      const int j = k / r;
-      const int rr = k - j * r;
+      int j, rr;
+      split(k0 + kl, j, rr);
       const int gcol = T.col0 + 8 * cv;
       const bool in = j < nslot && gcol < T.d_in;
       const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(
-          gA + (int64_t(s_exp[in ? j : 0]) * r + (in ? rr : 0)) * T.d_in + (in ? gcol : 0));
+          gA + ((uint32_t(s_exp[in ? j : 0]) * uint32_t(r) + uint32_t(in ? rr : 0)) * uint32_t(T.d_in) +
+                uint32_t(in ? gcol : 0)));
       sa[i] = in ? val : (u32x4){0u, 0u, 0u, 0u};
     }
   };
 
-  auto stage_store = [&]() {
+  auto stage_store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < B_VPT; ++i) {
       const int v = tid + 256 * i;
+      if (NBV % 256 != 0 && v >= NBV) break;
       const int row = v / (KC / 8);
       const int kv = v % (KC / 8);
-      const u32x4 o = rvec ? scale_bf16x8(sb[i], sc[i]) : sb[i];
-      *reinterpret_cast<u32x4*>(&Bs[row * LDK + 8 * kv]) = o;
+      if constexpr (rvec)
+        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = scale_bf16x8(sb[i], sc[i]);
+      else
+        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = sb[i];
     }
 #pragma unroll
     for (int i = 0; i < A_VPT; ++i) {
       const int v = tid + 256 * i;
+      if (NAV % 256 != 0 && v >= NAV) break;
       const int kl = v / (BN / 8);
       const int cv = v % (BN / 8);
-      const u32x4 x = sa[i];
-      uint16_t* col = &As[(8 * cv) * LDK + kl];
-      col[0 * LDK] = uint16_t(x.x);
-      col[1 * LDK] = uint16_t(x.x >> 16);
-      col[2 * LDK] = uint16_t(x.y);
-      col[3 * LDK] = uint16_t(x.y >> 16);
-      col[4 * LDK] = uint16_t(x.z);
-      col[5 * LDK] = uint16_t(x.z >> 16);
-      col[6 * LDK] = uint16_t(x.w);
-      col[7 * LDK] = uint16_t(x.w >> 16);
+      *reinterpret_cast<u32x4*>(&As[buf][kl * LDA + 8 * cv]) = sa[i];
     }
   };
 
-  // 4. first K chunk
-  stage_load(0);
-  stage_store();
-  __syncthreads();
+  // LDS element offsets of this lane's fragments inside a chunk buffer
+  //   B: row 16 RB wy + 16 rb + li, k 8 q (+ 32 ks)
+  //   A (transposed read): k row 8 q + (li / 4) (+ 4 for the upper half, + 32 ks),
+  //      columns 16 CT wx + 32 (ct / 2) + 4 (ct % 2) + 8 (li % 4) .. + 3
+  int boff[RB], aoff[CT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) boff[rb] = (16 * RB * wy + 16 * rb + li) * LDB + 8 * q;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+    aoff[ct] = (8 * q + (li >> 2)) * LDA + 16 * CT * wx + 32 * (ct >> 1) + 4 * (ct & 1) + 8 * (li & 3);
 
-  f32x4 acc[RB][4];
+  f32x4 acc[RB][CT];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[rb][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) acc[rb][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // LDS element offsets of this lane's operand fragments (k offset 8 q included)
-  int aoff[4], boff[RB];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int col = 64 * wx + 32 * (ct >> 1) + 8 * (li >> 2) + 4 * (ct & 1) + (li & 3);
-    aoff[ct] = col * LDK + 8 * q;
-  }
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) boff[rb] = (16 * RB * wy + 16 * rb + li) * LDK + 8 * q;
-
-  for (int k0 = 0;;) {
+  // 4. chunk 0, then the pipelined K loop (one barrier per chunk: chunk c+1 is
+  // written to the other buffer, which every wave finished reading at the previous
+  // barrier)
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunks;
+    if (more) stage_load((c + 1) * KC);
 #pragma unroll
     for (int ks = 0; ks < KC / 32; ++ks) {
-      bf16x8_t af[4], bfr[RB];
+      bf16x8_t af[CT], bfr[RB];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) af[ct] = *reinterpret_cast<const bf16x8_t*>(&As[aoff[ct] + 32 * ks]);
+      for (int ct = 0; ct < CT; ++ct) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)((lds_u16*)As[buf] + aoff[ct] + 32 * ks * LDA));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)((lds_u16*)As[buf] + aoff[ct] + (32 * ks + 4) * LDA));
+        const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        af[ct] = __builtin_bit_cast(bf16x8_t, both);
+      }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) bfr[rb] = *reinterpret_cast<const bf16x8_t*>(&Bs[boff[rb] + 32 * ks]);
+      for (int rb = 0; rb < RB; ++rb)
+        bfr[rb] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][boff[rb] + 32 * ks]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
           acc[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ct], bfr[rb], acc[rb][ct], 0, 0, 0);
     }
-    k0 += KC;
-    if (k0 >= kr) break;
-    __syncthreads();  // every wave is done reading this chunk
-    stage_load(k0);
-    stage_store();
-    __syncthreads();
+    if (more) {
+      stage_store(buf ^ 1);
+      __syncthreads();
+    }
   }
 
-  // 5. W + delta, one rounding to bf16, 16-byte stores
+  // 5. delta through LDS into the row-major layout of the W vectors: lane (q, i) of
+  //    block (rb, ct) holds 4 adjacent columns of one row (a 16-byte write); then
+  //    W + delta is rounded once and stored
+  __syncthreads();  // every wave is done reading the operand chunks the delta overwrites
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (!ok[rb][h]) continue;
-      const u32x4 w = wv[rb][h];
-      const f32x4 d0 = acc[rb][2 * h];
-      const f32x4 d1 = acc[rb][2 * h + 1];
-      u32x4 o;
-      o.x = pack_bf16x2(bf16_lo(w.x) + d0[0], bf16_hi(w.x) + d0[1]);
-      o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
-      o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
-      o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
-#if ADA_NT_STORE
-      __builtin_nontemporal_store(o, reinterpret_cast<ADA_GLOBAL u32x4*>(dst + woff[rb][h]));
-#else
-      *reinterpret_cast<ADA_GLOBAL u32x4*>(dst + woff[rb][h]) = o;
-#endif
+    for (int ct = 0; ct < CT; ++ct) {
+      const int row = 16 * RB * wy + 16 * rb + li;
+      const int col = 16 * CT * wx + 32 * (ct >> 1) + 8 * q + 4 * (ct & 1);
+      *reinterpret_cast<f32x4*>(&Ds[row * LDD + col]) = acc[rb][ct];
     }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    if (!ok[u]) continue;
+    const int v = tid + 256 * u;
+    const float* d = &Ds[(v / (BN / 8)) * LDD + 8 * (v % (BN / 8))];
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(d);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(d + 4);
+    const u32x4 w = wv[u];
+    u32x4 o;
+    o.x = pack_bf16x2(bf16_lo(w.x) + d0[0], bf16_hi(w.x) + d0[1]);
+    o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
+    o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
+    o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
+    *reinterpret_cast<ADA_GLOBAL u32x4*>(dst + woff[u]) = o;
   }
 }
 
@@ -488,16 +552,29 @@ __global__ void __launch_bounds__(256) merge_f32_kernel(MergeParams p) {
   }
 }
 
+template <int KC, class S>
+void launch_bf16(const MergeParams& p, dim3 grid, dim3 block, hipStream_t s) {
+  if (p.r_shift >= 0 && (p.r & 7) == 0)
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 0>), grid, block, 0, s, p);
+  else if ((p.r & 7) == 0)
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 1>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 2>), grid, block, 0, s, p);
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t s) {
   if (p.total_tiles <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(p.total_tiles)), block(256);
   if (dtype == 1) {
+    // the caller built p's work table for bf16_tile(kr_max)
     if (kr_max <= 32)
-      hipLaunchKernelGGL((merge_bf16_kernel<32, kBF16RowBlocks>), grid, block, 0, s, p);
+      launch_bf16<32, ShortTile>(p, grid, block, s);
+    else if (kr_max <= kLongKR)
+      launch_bf16<64, ShortTile>(p, grid, block, s);
     else
-      hipLaunchKernelGGL((merge_bf16_kernel<64, kBF16RowBlocks>), grid, block, 0, s, p);
+      launch_bf16<64, LongTile>(p, grid, block, s);
   } else {
     hipLaunchKernelGGL(merge_f32_kernel<32>, grid, block, 0, s, p);
   }
