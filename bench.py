@@ -157,13 +157,16 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.calibrate_copy:
+        # a plain streaming kernel of known traffic for scaling the HBM byte counters:
+        # out-of-place negation reads and writes exactly 2n bytes per launch
         n = args.calibrate_copy * (1 << 20) // 2
         a = torch.ones(n, dtype=torch.bfloat16, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes_read": 2 * n, "bytes_written": 2 * n, "launches": 3}))
+        print(json.dumps({"kernel": "neg", "bytes_read_per_launch": 2 * n, "bytes_written_per_launch": 2 * n,
+                          "launches": 3}))
         return
 
     cfg = PRESETS[args.workload]
