@@ -1,0 +1,74 @@
+"""Full-size parity: the 7B- and 70B-shaped stacks in the launch configuration the
+benchmark times (pregate, then one in-place merge launch over every layer and
+projection, then one unmerge launch), checked against the oracle on sampled rows of
+every projection and on every element of selected projections."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import (BF16_ATOL, BF16_RTOL, GATE_ATOL, GATE_RTOL, check_close, gapped_stack_router, sample_rows,
+                     to64)
+from oracle import adafuse as O
+from weight_merge_amd import api as A
+from weight_merge_amd import synth
+from weight_merge_amd.configs import LLAMA7B_E8R16K2, LLAMA7B_E16R64K4, LLAMA70B_E8R16K2
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_stack(cfg, seed, full_check):
+    """full_check(l, p, proj) -> True for the projections compared element by element."""
+    h, R, seed = gapped_stack_router(cfg, seed)
+    ridx, rg = O.pregate(to64(h), to64(R), cfg.k, cfg.renorm)
+    st = synth.make_stack(cfg, seed, device=DEV)
+    rng = np.random.default_rng(seed)
+    keep = []  # (l, p, rows, W rows before the merge)
+    for l, p, proj in st.items():
+        rows = np.arange(proj.d_out) if full_check(l, p, proj) else sample_rows(proj.d_out, rng)
+        keep.append((l, p, rows, st.W[l][p][torch.from_numpy(rows).to(DEV)].cpu()))
+    model = A.AdaModel([(st.W[l][p], None, st.A[l][p], st.B[l][p]) for l, p, _ in st.items()], cfg.E, cfg.r)
+    idx, gate = A.ada_pregate(h.to(DEV), R.to(DEV), cfg.k, cfg.renorm)
+    A.ada_merge(model, idx, gate, cfg.scale)
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == ridx.tolist()
+    check_close(gate, rg, GATE_RTOL, GATE_ATOL, "gates")
+
+    n_checked = 0
+    for l, p, rows, w0 in keep:
+        rows_t = torch.from_numpy(rows).to(DEV)
+        got = st.W[l][p][rows_t]
+        Bsel = st.B[l][p][:, rows_t, :]
+        ref = O.merge(to64(w0), to64(st.A[l][p]), to64(Bsel), ridx, rg, cfg.scale)
+        check_close(got, ref, BF16_RTOL, BF16_ATOL, f"merge layer {l} proj {cfg.projections[p].name}")
+        n_checked += got.numel()
+
+    A.ada_unmerge(model, idx, gate, cfg.scale)
+    torch.cuda.synchronize()
+    exact = total = 0
+    for l, p, rows, w0 in keep:
+        got = st.W[l][p][torch.from_numpy(rows).to(DEV)].cpu()
+        check_close(got, to64(w0), BF16_RTOL, BF16_ATOL, f"unmerge layer {l} proj {cfg.projections[p].name}")
+        exact += int((got.view(torch.int16) == w0.view(torch.int16)).sum())
+        total += got.numel()
+    model.destroy()
+    del st
+    torch.cuda.empty_cache()
+    print(f"{cfg.name}: {n_checked} merged elements checked, unmerge bit-exact fraction {exact / total:.4f}")
+    return exact / total
+
+
+def test_llama7b_e8r16k2_stack():
+    frac = run_stack(LLAMA7B_E8R16K2, 1000, lambda l, p, proj: l == 0)
+    assert frac > 0.8
+
+
+def test_llama7b_e16r64k4_stack():
+    frac = run_stack(LLAMA7B_E16R64K4, 2000, lambda l, p, proj: l == 31)
+    assert frac > 0.8
+
+
+def test_llama70b_e8r16k2_stack():
+    # element by element: the k and v projections (1024 x 8192) of layer 0
+    frac = run_stack(LLAMA70B_E8R16K2, 3000, lambda l, p, proj: l == 0 and proj.name in ("k", "v"))
+    assert frac > 0.8
