@@ -139,6 +139,153 @@ def cpu_baseline(cfg, seed, n_layers):
     }
 
 
+def time_ms(torch, fn, reps):
+    """Mean milliseconds of fn() over reps calls, HIP events on the current stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def simple_fusion_ms(torch, st, cfg, idx, gate, reps):
+    """The pages' ablation without the fused kernel: one library GEMM per projection,
+    W += (s g B_sel) @ A_sel with torch/hipBLASLt (224 launches plus gathers), then the
+    same to undo it; returns the mean ms of one such merge."""
+    sel = idx.long()
+    coef = (cfg.scale * gate).to(torch.bfloat16)
+
+    def merge(sign):
+        for l, p, _ in st.items():
+            Bs = st.B[l][p].index_select(0, sel) * (sign * coef).view(-1, 1, 1)   # k x d_out x r
+            Bcat = Bs.permute(1, 0, 2).reshape(Bs.shape[1], -1)                   # d_out x k r
+            Acat = st.A[l][p].index_select(0, sel).reshape(-1, st.A[l][p].shape[2])  # k r x d_in
+            st.W[l][p].addmm_(Bcat, Acat)
+
+    for _ in range(2):
+        merge(1.0)
+        merge(-1.0)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tot = 0.0
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e[0].record()
+        merge(1.0)
+        e[1].record()
+        merge(-1.0)
+        e[2].record()
+        torch.cuda.synchronize()
+        tot += e[0].elapsed_time(e[1])
+    return tot / reps
+
+
+def run_e2e(args, cfg, torch, A, synth, dev):
+    """End-to-end batch-1 request on the 7B-shaped stack: pregate + merge, decode steps
+    of one GEMV per projection through every layer, unmerge; against the unmerged
+    per-layer routed baseline (router + base GEMV + shrink + expand per projection,
+    every layer, every step) and the backbone alone.  Decode steps are timed eagerly
+    (Python-driven launches) and as one captured HIP graph per token."""
+    steps = cfg.decode_steps
+    st = synth.make_stack(cfg, args.seed, device=dev)
+    h, R = synth.router_inputs(cfg, args.seed)
+    h, R = h.to(dev), R.to(dev)
+    xs = synth.decode_inputs(cfg, args.seed, 1, device=dev)  # one token's activations (content does not change timing)
+    x = {name: xs[name][0].contiguous() for name in xs}
+    ys = [[torch.empty(proj.d_out, dtype=torch.bfloat16, device=dev) for proj in cfg.projections]
+          for _ in range(cfg.n_layers)]
+    model = A.AdaModel([(st.W[l][p], None, st.A[l][p], st.B[l][p]) for l, p, _ in st.items()], cfg.E, cfg.r)
+    idx = torch.empty(cfg.k, dtype=torch.int32, device=dev)
+    gate = torch.empty(cfg.k, dtype=torch.float32, device=dev)
+    lidx = [torch.empty(cfg.k, dtype=torch.int32, device=dev) for _ in range(cfg.n_layers)]
+    lgate = [torch.empty(cfg.k, dtype=torch.float32, device=dev) for _ in range(cfg.n_layers)]
+    ws = [[torch.empty((proj.d_out + cfg.kr + 3) // 4 * 4, dtype=torch.float32, device=dev)
+           for proj in cfg.projections] for _ in range(cfg.n_layers)]
+
+    def token_merged():
+        for l, p, proj in st.items():
+            A.ada_decode_gemv(st.W[l][p], x[proj.name], ys[l][p])
+
+    def token_baseline():
+        for l in range(cfg.n_layers):
+            A.ada_pregate(h, R, cfg.k, cfg.renorm, lidx[l], lgate[l])
+            for p, proj in enumerate(cfg.projections):
+                A.ada_lora_apply(st.W[l][p], st.A[l][p], st.B[l][p], lidx[l], lgate[l], cfg.scale, x[proj.name],
+                                 ys[l][p], ws[l][p])
+
+    def graph_of(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    reps = max(3, args.steps)
+    # AdaFuse: selection, merge, decode, unmerge
+    A.ada_pregate(h, R, cfg.k, cfg.renorm, idx, gate)
+    t_pregate = time_ms(torch, lambda: A.ada_pregate(h, R, cfg.k, cfg.renorm, idx, gate), 20)
+    pair = time_ms(torch, lambda: (A.ada_merge(model, idx, gate, cfg.scale), A.ada_unmerge(model, idx, gate, cfg.scale)), 5)
+    backbone_eager = time_ms(torch, token_merged, reps)      # on unmerged W: the backbone alone
+    g_backbone = graph_of(token_merged)
+    backbone_graph = time_ms(torch, g_backbone.replay, reps)
+    A.ada_merge(model, idx, gate, cfg.scale)
+    merged_eager = time_ms(torch, token_merged, reps)
+    g_merged = graph_of(token_merged)
+    merged_graph = time_ms(torch, g_merged.replay, reps)
+    A.ada_unmerge(model, idx, gate, cfg.scale)
+    base_eager = time_ms(torch, token_baseline, max(2, reps // 4))
+    g_base = graph_of(token_baseline)
+    base_graph = time_ms(torch, g_base.replay, reps)
+    del g_backbone, g_merged, g_base
+    simple = simple_fusion_ms(torch, st, cfg, idx, gate, 3)
+
+    launches_merged = cfg.n_layers * len(cfg.projections)
+    launches_base = cfg.n_layers * (1 + 3 * len(cfg.projections))
+    req_graph = t_pregate + pair + steps * merged_graph
+    req_base_graph = steps * base_graph
+    req_eager = t_pregate + pair + steps * merged_eager
+    req_base_eager = steps * base_eager
+    overhead = t_pregate + pair
+    be = None if base_graph <= merged_graph else overhead / (base_graph - merged_graph)
+    token_bytes = cfg.decode_bytes_per_token()
+    out = {
+        "metric": "end-to-end batch-1 request: ms per request and ms per decode token",
+        "value": round(req_graph, 3),
+        "unit": "ms/request (graph-captured decode)",
+        "higher_is_better": False,
+        "n_gpus": 1,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,.) draws on the device; no trained weights)",
+        "config": {"workload": cfg.note, "preset": cfg.name, "decode_steps": steps, "layers": cfg.n_layers,
+                   "E": cfg.E, "r": cfg.r, "k": cfg.k},
+        "ms": {
+            "pregate": round(t_pregate, 4),
+            "merge_plus_unmerge": round(pair, 3),
+            "token_backbone_graph": round(backbone_graph, 4),
+            "token_merged_graph": round(merged_graph, 4),
+            "token_baseline_graph": round(base_graph, 4),
+            "token_backbone_eager": round(backbone_eager, 4),
+            "token_merged_eager": round(merged_eager, 4),
+            "token_baseline_eager": round(base_eager, 4),
+            "request_adafuse_graph": round(req_graph, 3),
+            "request_baseline_graph": round(req_base_graph, 3),
+            "request_adafuse_eager": round(req_eager, 3),
+            "request_baseline_eager": round(req_base_eager, 3),
+            "simple_fusion_merge": round(simple, 3),
+        },
+        "decode_GBps_merged_graph": round(token_bytes / (merged_graph * 1e-3) / 1e9, 1),
+        "launches_per_token": {"merged": launches_merged, "baseline": launches_base},
+        "break_even_tokens_graph": None if be is None else round(be, 1),
+        "speedup_request_graph": round(req_base_graph / req_graph, 3),
+        "speedup_request_eager": round(req_base_eager / req_eager, 3),
+        "overhead_vs_backbone_graph": round(merged_graph / backbone_graph - 1, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -170,6 +317,8 @@ def main():
         return
 
     cfg = PRESETS[args.workload]
+    if cfg.decode_steps:
+        return run_e2e(args, cfg, torch, A, synth, dev)
     mode = "out_of_place" if args.out_of_place else "in_place"
     t_gen = time.perf_counter()
     st = synth.make_stack(cfg, args.seed, device=dev)

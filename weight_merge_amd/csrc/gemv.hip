@@ -54,42 +54,42 @@ __device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) {
 }
 __device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
 
-// Each wave owns ROWS consecutive rows and walks them with 16-byte loads, lanes
-// striding over the row; one butterfly per row at the end.
-template <typename T, int ROWS>
+// One row per wave, four rows per workgroup.  A lane walks its row with 16-byte loads
+// in batches of U vectors, all issued before any is used (U x 64 x 16 bytes in flight
+// per wave); the x vectors of the same columns come from L1/L2.  The batch tail is
+// branch-free: past the row end a lane re-reads the row's first vector and multiplies
+// it by a zero x vector.  One butterfly per row at the end.
+template <typename T, int U>
 __global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ W, int d_out, int d_in,
                                                    int64_t ld, const T* __restrict__ x,
                                                    T* __restrict__ y, float* __restrict__ y32) {
   constexpr int VEC = 16 / sizeof(T);
   const int lane = threadIdx.x & 63;
-  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
-  if (row0 >= d_out) return;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d_out) return;
   const int nvec = d_in / VEC;
-  const uint4* xv = reinterpret_cast<const uint4*>(x);
-  const uint4* wr[ROWS];
+  const uint4* __restrict__ xv = reinterpret_cast<const uint4*>(x);
+  const uint4* __restrict__ wr = reinterpret_cast<const uint4*>(W + int64_t(row) * ld);
+  float acc = 0.f;
+  for (int v0 = 0; v0 < nvec; v0 += 64 * U) {
+    uint4 wv[U], xx[U];
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    const int row = row0 + r < d_out ? row0 + r : d_out - 1;  // clamp: duplicate rows are discarded
-    wr[r] = reinterpret_cast<const uint4*>(W + int64_t(row) * ld);
-  }
-  float acc[ROWS];
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) acc[r] = 0.f;
-#pragma unroll 4
-  for (int v = lane; v < nvec; v += 64) {
-    const uint4 xx = xv[v];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) dot8(wr[r][v], xx, acc[r], T());
-  }
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    const float s = wave_sum(acc[r]);
-    if (lane == 0 && row0 + r < d_out) {
-      if (y32)
-        y32[row0 + r] = s;
-      else
-        store_out(y, row0 + r, s);
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + lane + 64 * u;
+      const bool in = v < nvec;
+      wv[u] = wr[in ? v : 0];
+      const uint4 xr = xv[in ? v : 0];
+      xx[u] = in ? xr : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) dot8(wv[u], xx[u], acc, T());
+  }
+  const float s = wave_sum(acc);
+  if (lane == 0) {
+    if (y32)
+      y32[row] = s;
+    else
+      store_out(y, row, s);
   }
 }
 
@@ -143,14 +143,13 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const T* __restrict__ 
 
 hipError_t launch_gemv(const void* w, int d_out, int d_in, int64_t ld, const void* x, void* y,
                        float* y32, int dtype, hipStream_t s) {
-  constexpr int ROWS = 2;
-  const dim3 grid((d_out + 4 * ROWS - 1) / (4 * ROWS)), block(256);
+  const dim3 grid((d_out + 3) / 4), block(256);
   if (dtype == 1)
-    hipLaunchKernelGGL((gemv_kernel<uint16_t, ROWS>), grid, block, 0, s, static_cast<const uint16_t*>(w),
-                       d_out, d_in, ld, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), y32);
+    hipLaunchKernelGGL((gemv_kernel<uint16_t, 8>), grid, block, 0, s, static_cast<const uint16_t*>(w), d_out,
+                       d_in, ld, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), y32);
   else
-    hipLaunchKernelGGL((gemv_kernel<float, ROWS>), grid, block, 0, s, static_cast<const float*>(w), d_out,
-                       d_in, ld, static_cast<const float*>(x), static_cast<float*>(y), y32);
+    hipLaunchKernelGGL((gemv_kernel<float, 8>), grid, block, 0, s, static_cast<const float*>(w), d_out, d_in,
+                       ld, static_cast<const float*>(x), static_cast<float*>(y), y32);
   return hipGetLastError();
 }
 
