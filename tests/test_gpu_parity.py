@@ -84,6 +84,10 @@ MERGE_CASES = [
     (6, 40, 3, 264, 392, "bf16", False),
     (8, 12, 8, 136, 264, "bf16", True),
     (8, 16, 4, 200, 136, "bf16", False),
+    # r a power of two and a multiple of the K chunk: one slot per chunk
+    (4, 64, 1, 136, 264, "bf16", True),
+    (6, 32, 1, 72, 136, "bf16", False),
+    (5, 128, 3, 200, 392, "bf16", True),
 ]
 
 

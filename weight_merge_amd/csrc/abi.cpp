@@ -12,6 +12,10 @@
 
 #include "common.h"
 
+#ifndef ADA_LONG_TILE_GROUP
+#define ADA_LONG_TILE_GROUP 8
+#endif
+
 namespace {
 
 constexpr uint64_t kModelMagic = 0x6164614675736521ull;
@@ -67,6 +71,7 @@ int launch_merge_common(ada_model m, const ada::Selection& s0, const ada::Select
   p.r_shift = (m->r & (m->r - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(m->r)) : -1;
   p.src_is_out = src_is_out;
   p.xcd_remap = 1;
+  p.tile_group = m->dtype == ADA_BF16 && kr_max > ada::kLongKR ? ADA_LONG_TILE_GROUP : 1;
   const hipError_t e = ada::launch_merge(p, m->dtype, kr_max, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADA_OK : ADA_EHIP;
 }

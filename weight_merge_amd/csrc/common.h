@@ -69,6 +69,7 @@ struct MergeParams {
   int32_t r_shift;     // log2(r) when r is a power of two, else -1
   int32_t src_is_out;  // 1: read the merged buffer (w_out) instead of w
   int32_t xcd_remap;   // 1: give each XCD a contiguous range of tiles
+  int32_t tile_group;  // row bands walked down one column block before moving right
 };
 
 hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t s);

@@ -130,6 +130,21 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
   const MergeEntry* en = p.table + e;
   const int64_t local = t - en->tile_base;
   const int tn = en->tiles_n;
+  // Tile order inside a projection: groups of tile_group row bands, each group walked
+  // column block by column block (down the group's bands first).  tile_group = 1 is
+  // plain row-major order.  Larger groups let consecutive tiles share an A_cat column
+  // slab and keep the group's B_cat rows in L2, which matters when k*r is large.
+  int band, cblk;
+  {
+    const int G = p.tile_group;
+    const int tm = en->tiles_m;
+    const int grp = int(local / (int64_t(G) * tn));
+    const int first = grp * G;
+    const int gsize = min(G, tm - first);
+    const int within = int(local - int64_t(grp) * G * tn);
+    band = first + within % gsize;
+    cblk = within / gsize;
+  }
   TileRef r;
   r.src = p.src_is_out ? en->w_out : en->w;
   r.dst = en->w_out;
@@ -138,8 +153,8 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
   r.ld = en->ld;
   r.d_out = en->d_out;
   r.d_in = en->d_in;
-  r.row0 = int(local / tn) * tile_rows;
-  r.col0 = int(local % tn) * tile_cols;
+  r.row0 = band * tile_rows;
+  r.col0 = cblk * tile_cols;
   return r;
 }
 
@@ -174,6 +189,8 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 //   0: r a power of two and a multiple of 8 (shifts; 16-byte B vectors)
 //   1: r a multiple of 8 (division; 16-byte B vectors)
 //   2: any other r (division; B element by element)
+//   3: r a power of two and a multiple of KC: every chunk lies inside one slot, so the
+//      slot, its coefficient and its base addresses are uniform per chunk
 #ifndef ADA_WAVES_PER_EU
 #define ADA_WAVES_PER_EU 1
 #endif
@@ -183,7 +200,11 @@ merge_bf16_kernel(MergeParams p) {
   constexpr int WGM = 4 / WGN;
   constexpr int BM = 16 * RB * WGM, BN = 16 * CT * WGN;
   constexpr int LDB = KC + 8;   // Bs row pitch (elements)
-  constexpr int LDA = BN + 8;   // As row pitch (elements)
+  // As row pitch: BN + 32 elements is 16 (mod 64) banks, so the 16 lanes of a
+  // transposed read (4 k rows x 4 column chunks) touch 16 disjoint bank pairs; the
+  // short-contraction tiles read A once per tile and keep the smaller pitch, whose
+  // LDS footprint stays under the delta tile's
+  constexpr int LDA = BN + (RB >= 4 ? 32 : 8);
   constexpr int NBV = BM * KC / 8;  // 16-byte B vectors per chunk
   constexpr int NAV = KC * BN / 8;  // 16-byte A vectors per chunk
   constexpr int B_VPT = (NBV + 255) / 256;
@@ -307,7 +328,49 @@ merge_bf16_kernel(MergeParams p) {
   float sc[B_VPT];
   u32x4 sa[A_VPT];
 
+  // RMODE 3: per-thread parts of the gather offsets, fixed across chunks
+  uint32_t b_off3[B_VPT], a_off3[A_VPT];
+  bool b_ok3[B_VPT], a_ok3[A_VPT];
+  if constexpr (RMODE == 3) {
+#pragma unroll
+    for (int i = 0; i < B_VPT; ++i) {
+      const int v = tid + 256 * i;
+      const int grow = T.row0 + v / (KC / 8);
+      b_ok3[i] = grow < T.d_out;
+      b_off3[i] = uint32_t(b_ok3[i] ? grow : 0) * uint32_t(r) + 8u * uint32_t(v % (KC / 8));
+    }
+#pragma unroll
+    for (int i = 0; i < A_VPT; ++i) {
+      const int v = tid + 256 * i;
+      const int gcol = T.col0 + 8 * (v % (BN / 8));
+      a_ok3[i] = gcol < T.d_in;
+      a_off3[i] = uint32_t(v / (BN / 8)) * uint32_t(T.d_in) + uint32_t(a_ok3[i] ? gcol : 0);
+    }
+  }
+
   auto stage_load = [&](int k0) {
+    if constexpr (RMODE == 3) {
+      const int j = k0 >> r_shift;  // < nslot: the chunks tile the contraction exactly
+      const int rr0 = k0 & (r - 1);
+      const int e = __builtin_amdgcn_readfirstlane(s_exp[j]);
+      const float c = s_coef[j];
+      const ADA_GLOBAL uint16_t* bj = gB + uint32_t(e) * uint32_t(T.d_out) * uint32_t(r) + uint32_t(rr0);
+      const ADA_GLOBAL uint16_t* aj = gA + (uint32_t(e) * uint32_t(r) + uint32_t(rr0)) * uint32_t(T.d_in);
+#pragma unroll
+      for (int i = 0; i < B_VPT; ++i) {
+        if (NBV % 256 != 0 && tid + 256 * i >= NBV) break;
+        const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(bj + b_off3[i]);
+        sb[i] = val & (u32x4)(0u - uint32_t(b_ok3[i]));
+        sc[i] = c;
+      }
+#pragma unroll
+      for (int i = 0; i < A_VPT; ++i) {
+        if (NAV % 256 != 0 && tid + 256 * i >= NAV) break;
+        const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(aj + a_off3[i]);
+        sa[i] = val & (u32x4)(0u - uint32_t(a_ok3[i]));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < B_VPT; ++i) {
       const int v = tid + 256 * i;
@@ -323,7 +386,9 @@ merge_bf16_kernel(MergeParams p) {
         const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(
             gB + ((uint32_t(s_exp[js]) * uint32_t(T.d_out) + uint32_t(in ? grow : 0)) * uint32_t(r) +
                   uint32_t(in ? rr : 0)));
-        sb[i] = in ? val : (u32x4){0u, 0u, 0u, 0u};
+        // a mask, not a select: a select of a load lets the compiler sink the load into
+        // an exec-masked block of its own
+        sb[i] = val & (u32x4)(0u - uint32_t(in));
         sc[i] = s_coef[js];
       } else {
         // rank not a multiple of 8: element by element, coefficient applied here
@@ -356,7 +421,7 @@ merge_bf16_kernel(MergeParams p) {
       const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(
           gA + ((uint32_t(s_exp[in ? j : 0]) * uint32_t(r) + uint32_t(in ? rr : 0)) * uint32_t(T.d_in) +
                 uint32_t(in ? gcol : 0)));
-      sa[i] = in ? val : (u32x4){0u, 0u, 0u, 0u};
+      sa[i] = val & (u32x4)(0u - uint32_t(in));
     }
   };
 
@@ -554,7 +619,9 @@ __global__ void __launch_bounds__(256) merge_f32_kernel(MergeParams p) {
 
 template <int KC, class S>
 void launch_bf16(const MergeParams& p, dim3 grid, dim3 block, hipStream_t s) {
-  if (p.r_shift >= 0 && (p.r & 7) == 0)
+  if (p.r_shift >= 0 && p.r % KC == 0)
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 3>), grid, block, 0, s, p);
+  else if (p.r_shift >= 0 && (p.r & 7) == 0)
     hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 0>), grid, block, 0, s, p);
   else if ((p.r & 7) == 0)
     hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 1>), grid, block, 0, s, p);
