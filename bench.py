@@ -215,6 +215,16 @@ def run_e2e(args, cfg, torch, A, synth, dev):
                 A.ada_lora_apply(st.W[l][p], st.A[l][p], st.B[l][p], lidx[l], lgate[l], cfg.scale, x[proj.name],
                                  ys[l][p], ws[l][p])
 
+    lws = [torch.empty(A.lora_layer_workspace_elems([p.d_out for p in cfg.projections], cfg.k, cfg.r),
+                       dtype=torch.float32, device=dev) for _ in range(cfg.n_layers)]
+
+    def token_baseline_fused():
+        # the strongest unmerged comparator: router + two launches per layer
+        for l in range(cfg.n_layers):
+            A.ada_pregate(h, R, cfg.k, cfg.renorm, lidx[l], lgate[l])
+            A.ada_lora_layer([(st.W[l][p], st.A[l][p], st.B[l][p], x[proj.name], ys[l][p])
+                              for p, proj in enumerate(cfg.projections)], lidx[l], lgate[l], cfg.scale, lws[l])
+
     def graph_of(fn):
         fn()
         torch.cuda.synchronize()
@@ -236,10 +246,34 @@ def run_e2e(args, cfg, torch, A, synth, dev):
     g_merged = graph_of(token_merged)
     merged_graph = time_ms(torch, g_merged.replay, reps)
     A.ada_unmerge(model, idx, gate, cfg.scale)
+    # N1: fused switch between two selections (undo prev + apply cur in one pass), and
+    # N2: switching every decode token (each token pays a full switch)
+    h2, R2 = synth.router_inputs(cfg, args.seed + 1)
+    h2 = h2.to(dev)
+    idx2 = torch.empty(cfg.k, dtype=torch.int32, device=dev)
+    gate2 = torch.empty(cfg.k, dtype=torch.float32, device=dev)
+    A.ada_pregate(h2, R, cfg.k, cfg.renorm, idx2, gate2)
+    A.ada_merge(model, idx, gate, cfg.scale)
+    sel = [(idx, gate), (idx2, gate2)]
+    flip = [0]
+
+    def switch_once():
+        a, b = sel[flip[0]], sel[1 - flip[0]]
+        A.ada_switch(model, a, b, cfg.scale)
+        flip[0] = 1 - flip[0]
+
+    t_switch = time_ms(torch, switch_once, 6)
+    per_token_switch = time_ms(torch, lambda: (switch_once(), token_merged()), reps)
+    if flip[0]:
+        switch_once()
+    A.ada_unmerge(model, idx, gate, cfg.scale)
     base_eager = time_ms(torch, token_baseline, max(2, reps // 4))
     g_base = graph_of(token_baseline)
     base_graph = time_ms(torch, g_base.replay, reps)
-    del g_backbone, g_merged, g_base
+    fused_eager = time_ms(torch, token_baseline_fused, max(2, reps // 2))
+    g_fused = graph_of(token_baseline_fused)
+    fused_graph = time_ms(torch, g_fused.replay, reps)
+    del g_backbone, g_merged, g_base, g_fused
     simple = simple_fusion_ms(torch, st, cfg, idx, gate, 3)
 
     launches_merged = cfg.n_layers * len(cfg.projections)
@@ -270,14 +304,22 @@ def run_e2e(args, cfg, torch, A, synth, dev):
             "token_backbone_eager": round(backbone_eager, 4),
             "token_merged_eager": round(merged_eager, 4),
             "token_baseline_eager": round(base_eager, 4),
+            "token_fused_unmerged_graph": round(fused_graph, 4),
+            "token_fused_unmerged_eager": round(fused_eager, 4),
+            "request_fused_unmerged_graph": round(steps * fused_graph, 3),
             "request_adafuse_graph": round(req_graph, 3),
             "request_baseline_graph": round(req_base_graph, 3),
             "request_adafuse_eager": round(req_eager, 3),
             "request_baseline_eager": round(req_base_eager, 3),
             "simple_fusion_merge": round(simple, 3),
+            "switch": round(t_switch, 3),
+            "token_with_switch_eager": round(per_token_switch, 4),
+            "request_switch_every_token_eager": round(steps * per_token_switch + t_pregate, 3),
         },
         "decode_GBps_merged_graph": round(token_bytes / (merged_graph * 1e-3) / 1e9, 1),
-        "launches_per_token": {"merged": launches_merged, "baseline": launches_base},
+        "launches_per_token": {"merged": launches_merged, "baseline": launches_base,
+                               "fused_unmerged": cfg.n_layers * 3},
+        "speedup_request_vs_fused_unmerged_graph": round(steps * fused_graph / req_graph, 3),
         "break_even_tokens_graph": None if be is None else round(be, 1),
         "speedup_request_graph": round(req_base_graph / req_graph, 3),
         "speedup_request_eager": round(req_base_eager / req_eager, 3),

@@ -84,8 +84,9 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
  * enqueued merge has completed. */
 void ada_model_destroy(ada_model m);
 
-/* Number of 128x128 output tiles one merge launch of this model covers (for
- * measurement); negative status on a bad handle. */
+/* Number of output tiles one short-contraction merge launch of this model covers
+ * (64 x 128 tiles for bf16, 64 x 64 for fp32; for measurement); negative status on
+ * a bad handle. */
 int64_t ada_model_tiles(ada_model m);
 
 /*
@@ -154,6 +155,31 @@ int ada_lora_apply(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w,
                    const int32_t* idx, const float* gate, int32_t k, float scale,
                    const void* x, void* y, void* workspace, int64_t workspace_bytes,
                    int32_t dtype, void* stream);
+
+/* One projection of a layer for ada_lora_layer. */
+typedef struct {
+  const void* w;    /* [d_out][ld_w] base weights                   */
+  const void* a;    /* [E][r][d_in] down projections                */
+  const void* b;    /* [E][d_out][r] up projections                 */
+  const void* x;    /* [d_in] input                                  */
+  void* y;          /* [d_out] output                                */
+  int32_t d_out;
+  int32_t d_in;
+  int64_t ld_w;
+} ada_lora_proj;
+
+/*
+ * One layer of the unmerged, routed path for up to 16 projections in two launches
+ * (the same arithmetic as ada_lora_apply per projection, bit for bit): one grid
+ * computes every projection's base-GEMV rows and shrink rows A[idx_j] x, one grid
+ * every expand.  This is the strongest unmerged comparator for the merged path
+ * ([pt] technical summary 1: several kernel calls per layer in the conventional
+ * design).  All projections share E, r, the selection and the dtype.  `workspace`:
+ * caller-owned device memory of at least sum_p (d_out_p + k*r) * 4 bytes.
+ */
+int ada_lora_layer(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_t r,
+                   const int32_t* idx, const float* gate, int32_t k, float scale,
+                   void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* ada_status_string(int status);

@@ -10,6 +10,17 @@ from weight_merge_amd import _lib
 from weight_merge_amd._lib import (ADA_BF16, ADA_EALIGN, ADA_EDTYPE, ADA_EINVAL, ADA_ESHAPE, ADA_F32,
                                    AdaProj)
 
+# These calls pass fake pointers and must fail validation before any HIP call; where a
+# GPU is visible, a mistake in a test case would launch a kernel on them, so the
+# module only runs where none is.
+try:
+    import torch
+
+    _gpu = torch.cuda.is_available()
+except Exception:  # pragma: no cover
+    _gpu = False
+pytestmark = pytest.mark.skipif(_gpu, reason="fake-pointer validation tests run where no GPU is visible")
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "adafuse.h")
 
@@ -144,3 +155,26 @@ def test_lora_apply_validation(lib):
     assert call(6, 0) == ADA_ESHAPE    # E
     assert call(10, 5) == ADA_ESHAPE   # k > E
     assert call(15, 64 * 4) == ADA_ESHAPE  # workspace too small
+
+
+def test_lora_layer_validation(lib):
+    from weight_merge_amd._lib import AdaLoraProj
+    good = dict(w=P, a=P2, b=P, x=P2, y=P, d_out=64, d_in=64, ld_w=64)
+
+    def arr(**kw):
+        a = dict(good, **kw)
+        return (AdaLoraProj * 1)(AdaLoraProj(a["w"], a["a"], a["b"], a["x"], a["y"], a["d_out"], a["d_in"], a["ld_w"]))
+
+    f = lib.ada_lora_layer
+    ws = (64 + 2 * 8) * 4  # exactly what one 64-row projection with k*r = 16 needs
+    assert f(None, 1, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(), 1, 4, 8, None, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(), 1, 4, 8, P, P2, 2, 2.0, P, ws, 5, None) == ADA_EDTYPE
+    assert f(arr(), 0, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 17, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 1, 4, 8, P, P2, 5, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(x=None), 1, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(y=MIS), 1, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EALIGN
+    assert f(arr(d_in=60), 1, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 1, 4, 8, P, P2, 2, 2.0, P, ws - 16, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 1, 4, 8, P, P2, 2, 2.0, MIS, ws, ADA_BF16, None) == ADA_EALIGN

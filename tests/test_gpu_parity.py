@@ -389,3 +389,28 @@ def test_live_model_rejects_bad_selections():
     m.destroy()
     with pytest.raises(RuntimeError):
         A.ada_merge(m, idx, gate, 2.0)
+
+
+# ---------------------------------------------------------------- fused unmerged layer (comparator)
+
+
+@pytest.mark.parametrize("dt,E,r,k", [("bf16", 8, 16, 2), ("bf16", 16, 64, 4), ("fp32", 4, 8, 2)])
+def test_lora_layer_matches_oracle_and_the_three_launch_path(dt, E, r, k):
+    shapes = [(264, 520), (1032, 264), (8, 8), (520, 1032), (136, 136)]
+    idx, gate = make_selection(E, k, 64, dt, 12)
+    banks = [synth.adapter_bank(200 + i, E, r, do, di, dt) for i, (do, di) in enumerate(shapes)]
+    xs = [synth.host_normal(synth.tensor_seed(300 + i, di), (di,), 1.0, dt) for i, (_, di) in enumerate(shapes)]
+    dev = [(W.to(DEV), Aw.to(DEV), Bw.to(DEV), x.to(DEV)) for (W, Aw, Bw), x in zip(banks, xs)]
+    ys = [torch.full((W.shape[0],), float("nan"), dtype=TD[dt], device=DEV) for W, _, _ in banks]
+    A.ada_lora_layer([(w, a, b, x, y) for (w, a, b, x), y in zip(dev, ys)], idx.to(DEV), gate.to(DEV), 2.0)
+    ref3 = [A.ada_lora_apply(w, a, b, idx.to(DEV), gate.to(DEV), 2.0, x) for w, a, b, x in dev]
+    sync()
+    for (W, Aw, Bw), x, y, y3 in zip(banks, xs, ys, ref3):
+        assert torch.equal(y.cpu().view(torch.int16 if dt == "bf16" else torch.int32),
+                           y3.cpu().view(torch.int16 if dt == "bf16" else torch.int32))
+        ref = O.routed_lora_forward(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64),
+                                    2.0, to64(x))
+        W64, x64 = to64(W), to64(x)
+        mag = np.abs(W64) @ np.abs(x64)
+        err = np.abs(to64(y) - ref)
+        assert np.all(err <= gemv_bound(W64, x64, ref, dt) + 1e-4 * mag), float(err.max())

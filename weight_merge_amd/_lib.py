@@ -27,6 +27,19 @@ class AdaProj(ctypes.Structure):
     ]
 
 
+class AdaLoraProj(ctypes.Structure):
+    _fields_ = [
+        ("w", c_void_p),
+        ("a", c_void_p),
+        ("b", c_void_p),
+        ("x", c_void_p),
+        ("y", c_void_p),
+        ("d_out", c_int32),
+        ("d_in", c_int32),
+        ("ld_w", c_int64),
+    ]
+
+
 _SIGNATURES = {
     "ada_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ada_model_create": (ctypes.c_int, [ctypes.POINTER(AdaProj), c_int32, c_int32, c_int32, c_int32,
@@ -44,6 +57,8 @@ _SIGNATURES = {
     "ada_lora_apply": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_void_p, c_int32,
                                       c_int32, c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p,
                                       c_void_p, c_int64, c_int32, c_void_p]),
+    "ada_lora_layer": (ctypes.c_int, [ctypes.POINTER(AdaLoraProj), c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                      c_int32, c_float, c_void_p, c_int64, c_int32, c_void_p]),
 }
 
 _lib = None

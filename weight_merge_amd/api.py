@@ -12,7 +12,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import ADA_BF16, ADA_F32, AdaProj
+from ._lib import ADA_BF16, ADA_F32, AdaLoraProj, AdaProj
 
 _DT = {torch.float32: ADA_F32, torch.bfloat16: ADA_BF16}
 
@@ -196,3 +196,39 @@ def ada_lora_apply(w, a, b, idx, gate, scale: float, x, y=None, workspace=None, 
                                     _dtype(w), _stream(stream))
     _check(st, "ada_lora_apply")
     return y
+
+
+def lora_layer_workspace_elems(d_outs, k: int, r: int) -> int:
+    """fp32 elements of workspace ada_lora_layer needs for these projections."""
+    n = 0
+    for d in d_outs:
+        n = (n + d + k * r + 3) // 4 * 4
+    return n
+
+
+def ada_lora_layer(projs, idx, gate, scale: float, workspace=None, stream=None):
+    """One layer of the unmerged routed path (two launches for all projections).
+
+    projs: list of (w, a, b, x, y) with w [d_out, d_in], a [E, r, d_in], b [E, d_out, r],
+    x [d_in], y [d_out] (written)."""
+    projs = list(projs)
+    w0, a0 = projs[0][0], projs[0][1]
+    E, r, _ = a0.shape
+    pi, pg, k = _sel(idx, gate)
+    arr = (AdaLoraProj * len(projs))()
+    for i, (w, a, b, x, y) in enumerate(projs):
+        d_out, d_in = w.shape
+        if w.stride(1) != 1:
+            raise ValueError("w must have unit column stride")
+        for t, n in ((a, "a"), (b, "b"), (x, "x"), (y, "y")):
+            _contig(t, n)
+        if a.shape != (E, r, d_in) or b.shape != (E, d_out, r) or x.shape != (d_in,) or y.shape != (d_out,):
+            raise ValueError("projection shapes do not match")
+        arr[i] = AdaLoraProj(_dev(w, "w"), _dev(a, "a"), _dev(b, "b"), _dev(x, "x"), _dev(y, "y"), d_out, d_in,
+                             w.stride(0))
+    need = lora_layer_workspace_elems([p[0].shape[0] for p in projs], k, r)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.float32, device=w0.device)
+    st = _lib.load().ada_lora_layer(arr, len(projs), E, r, pi, pg, k, float(scale), _dev(workspace, "workspace"),
+                                    workspace.numel() * workspace.element_size(), _dtype(w0), _stream(stream))
+    _check(st, "ada_lora_layer")

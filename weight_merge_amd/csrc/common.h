@@ -87,4 +87,33 @@ hipError_t launch_lora_expand(const void* b, int E, int r, int d_out, const int3
                               const float* gate, int k, float scale, const float* y32,
                               const float* t, void* y, int dtype, hipStream_t s);
 
+// One layer of the unmerged routed path (at most kMaxLayerProj projections, passed
+// by value so the launch needs no device table).
+constexpr int kMaxLayerProj = 16;
+struct LoraLayerProj {
+  const void* w;
+  const void* a;
+  const void* b;
+  const void* x;
+  void* y;
+  int64_t ld;
+  int32_t d_out;
+  int32_t d_in;
+  int32_t dot_row0;  // first row of this projection in the stacked [W; A_sel] grid
+  int32_t out_row0;  // first output row of this projection in the expand grid
+  int64_t ws_off;    // fp32 workspace: d_out GEMV sums, then k*r shrink sums
+};
+struct LoraLayerParams {
+  LoraLayerProj proj[kMaxLayerProj];
+  int32_t n;
+  int32_t E;
+  int32_t r;
+  int32_t k;
+  const int32_t* idx;
+  const float* gate;
+  float scale;
+  float* ws;
+};
+hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s);
+
 }  // namespace ada

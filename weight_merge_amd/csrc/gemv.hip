@@ -54,22 +54,18 @@ __device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) {
 }
 __device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
 
-// One row per wave, four rows per workgroup.  A lane walks its row with 16-byte loads
+// Dot product of one row with x by one wave: a lane walks the row with 16-byte loads
 // in batches of U vectors, all issued before any is used (U x 64 x 16 bytes in flight
 // per wave); the x vectors of the same columns come from L1/L2.  The batch tail is
 // branch-free: past the row end a lane re-reads the row's first vector and multiplies
-// it by a zero x vector.  One butterfly per row at the end.
+// it by a zero x vector.  One butterfly at the end (every lane gets the sum).
 template <typename T, int U>
-__global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ W, int d_out, int d_in,
-                                                   int64_t ld, const T* __restrict__ x,
-                                                   T* __restrict__ y, float* __restrict__ y32) {
+__device__ __forceinline__ float row_dot(const T* __restrict__ rowp, const T* __restrict__ x, int d_in) {
   constexpr int VEC = 16 / sizeof(T);
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= d_out) return;
   const int nvec = d_in / VEC;
   const uint4* __restrict__ xv = reinterpret_cast<const uint4*>(x);
-  const uint4* __restrict__ wr = reinterpret_cast<const uint4*>(W + int64_t(row) * ld);
+  const uint4* __restrict__ wr = reinterpret_cast<const uint4*>(rowp);
   float acc = 0.f;
   for (int v0 = 0; v0 < nvec; v0 += 64 * U) {
     uint4 wv[U], xx[U];
@@ -84,7 +80,20 @@ __global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ W, int 
 #pragma unroll
     for (int u = 0; u < U; ++u) dot8(wv[u], xx[u], acc, T());
   }
-  const float s = wave_sum(acc);
+  return wave_sum(acc);
+}
+
+constexpr int kGemvBatch = 8;
+
+// One row per wave, four rows per workgroup.
+template <typename T>
+__global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ W, int d_out, int d_in,
+                                                   int64_t ld, const T* __restrict__ x,
+                                                   T* __restrict__ y, float* __restrict__ y32) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= d_out) return;
+  const float s = row_dot<T, kGemvBatch>(W + int64_t(row) * ld, x, d_in);
   if (lane == 0) {
     if (y32)
       y32[row] = s;
@@ -99,34 +108,22 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const T* __restrict__ 
                                                           int d_in, const int32_t* __restrict__ idx,
                                                           int k, const T* __restrict__ x,
                                                           float* __restrict__ t) {
-  constexpr int VEC = 16 / sizeof(T);
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= k * r) return;
   const int j = row / r, rr = row - j * r;
   const int e = idx[j];
   float acc = 0.f;
-  if (e >= 0 && e < E) {
-    const uint4* ar = reinterpret_cast<const uint4*>(A + (int64_t(e) * r + rr) * d_in);
-    const uint4* xv = reinterpret_cast<const uint4*>(x);
-    const int nvec = d_in / VEC;
-    for (int v = lane; v < nvec; v += 64) dot8(ar[v], xv[v], acc, T());
-  }
-  acc = wave_sum(acc);
+  if (e >= 0 && e < E) acc = row_dot<T, kGemvBatch>(A + (int64_t(e) * r + rr) * d_in, x, d_in);
   if (lane == 0) t[row] = acc;
 }
 
-// y[i] = RNE(y32[i] + sum_j scale * gate[j] * sum_rr B[idx_j][i][rr] t[j*r + rr]).
+// RNE(y32[i] + sum_j scale * gate[j] * sum_rr B[idx_j][i][rr] t[j*r + rr]) for one row i.
 template <typename T>
-__global__ void __launch_bounds__(256) lora_expand_kernel(const T* __restrict__ B, int E, int r,
-                                                          int d_out, const int32_t* __restrict__ idx,
-                                                          const float* __restrict__ gate, int k,
-                                                          float scale, const float* __restrict__ y32,
-                                                          const float* __restrict__ t,
-                                                          T* __restrict__ y) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= d_out) return;
-  float acc = y32[i];
+__device__ __forceinline__ float expand_row(const T* __restrict__ B, int E, int r, int d_out, int i,
+                                            const int32_t* __restrict__ idx, const float* __restrict__ gate,
+                                            int k, float scale, float y32, const float* __restrict__ t) {
+  float acc = y32;
   for (int j = 0; j < k; ++j) {
     const int e = idx[j];
     const float c = scale * gate[j];
@@ -136,7 +133,61 @@ __global__ void __launch_bounds__(256) lora_expand_kernel(const T* __restrict__ 
     for (int rr = 0; rr < r; ++rr) s = fmaf(load_elem(br, rr), t[j * r + rr], s);
     acc = fmaf(c, s, acc);
   }
-  store_out(y, i, acc);
+  return acc;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) lora_expand_kernel(const T* __restrict__ B, int E, int r,
+                                                          int d_out, const int32_t* __restrict__ idx,
+                                                          const float* __restrict__ gate, int k,
+                                                          float scale, const float* __restrict__ y32,
+                                                          const float* __restrict__ t,
+                                                          T* __restrict__ y) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d_out) return;
+  store_out(y, i, expand_row(B, E, r, d_out, i, idx, gate, k, scale, y32[i], t));
+}
+
+// ---- one layer of the unmerged routed path in two launches (the projections of a
+// layer are independent given their inputs): grid 1 computes every projection's base
+// GEMV rows and shrink rows, grid 2 every projection's expand.
+template <typename T>
+__global__ void __launch_bounds__(256) lora_layer_dot_kernel(LoraLayerParams p) {
+  const int lane = threadIdx.x & 63;
+  int g = blockIdx.x * 4 + (threadIdx.x >> 6);  // row of the stacked [W_p; A_sel,p] over p
+  int q = 0;
+  while (q < p.n - 1 && g >= p.proj[q + 1].dot_row0) ++q;
+  const LoraLayerProj& P = p.proj[q];
+  const int lr = g - P.dot_row0;
+  const int kr = p.k * p.r;
+  if (lr >= P.d_out + kr) return;
+  const T* x = static_cast<const T*>(P.x);
+  float* ws = p.ws + P.ws_off;
+  if (lr < P.d_out) {
+    const float s = row_dot<T, kGemvBatch>(static_cast<const T*>(P.w) + int64_t(lr) * P.ld, x, P.d_in);
+    if (lane == 0) ws[lr] = s;
+  } else {
+    const int sr = lr - P.d_out, j = sr / p.r, rr = sr - j * p.r;
+    const int e = p.idx[j];
+    float s = 0.f;
+    if (e >= 0 && e < p.E)
+      s = row_dot<T, kGemvBatch>(static_cast<const T*>(P.a) + (int64_t(e) * p.r + rr) * P.d_in, x, P.d_in);
+    if (lane == 0) ws[P.d_out + sr] = s;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) lora_layer_expand_kernel(LoraLayerParams p) {
+  const int g = blockIdx.x * 256 + threadIdx.x;  // output row over the concatenated projections
+  int q = 0;
+  while (q < p.n - 1 && g >= p.proj[q + 1].out_row0) ++q;
+  const LoraLayerProj& P = p.proj[q];
+  const int i = g - P.out_row0;
+  if (i >= P.d_out) return;
+  const float* ws = p.ws + P.ws_off;
+  store_out(static_cast<T*>(P.y), i,
+            expand_row(static_cast<const T*>(P.b), p.E, p.r, P.d_out, i, p.idx, p.gate, p.k, p.scale, ws[i],
+                       ws + P.d_out));
 }
 
 }  // namespace
@@ -145,10 +196,10 @@ hipError_t launch_gemv(const void* w, int d_out, int d_in, int64_t ld, const voi
                        float* y32, int dtype, hipStream_t s) {
   const dim3 grid((d_out + 3) / 4), block(256);
   if (dtype == 1)
-    hipLaunchKernelGGL((gemv_kernel<uint16_t, 8>), grid, block, 0, s, static_cast<const uint16_t*>(w), d_out,
+    hipLaunchKernelGGL((gemv_kernel<uint16_t>), grid, block, 0, s, static_cast<const uint16_t*>(w), d_out,
                        d_in, ld, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), y32);
   else
-    hipLaunchKernelGGL((gemv_kernel<float, 8>), grid, block, 0, s, static_cast<const float*>(w), d_out, d_in,
+    hipLaunchKernelGGL((gemv_kernel<float>), grid, block, 0, s, static_cast<const float*>(w), d_out, d_in,
                        ld, static_cast<const float*>(x), static_cast<float*>(y), y32);
   return hipGetLastError();
 }
@@ -175,6 +226,18 @@ hipError_t launch_lora_expand(const void* b, int E, int r, int d_out, const int3
   else
     hipLaunchKernelGGL(lora_expand_kernel<float>, grid, block, 0, s, static_cast<const float*>(b), E, r,
                        d_out, idx, gate, k, scale, y32, t, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s) {
+  const dim3 g1((dot_rows + 3) / 4), g2((out_rows + 255) / 256), block(256);
+  if (dtype == 1) {
+    hipLaunchKernelGGL(lora_layer_dot_kernel<uint16_t>, g1, block, 0, s, p);
+    hipLaunchKernelGGL(lora_layer_expand_kernel<uint16_t>, g2, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL(lora_layer_dot_kernel<float>, g1, block, 0, s, p);
+    hipLaunchKernelGGL(lora_layer_expand_kernel<float>, g2, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
