@@ -636,10 +636,10 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t
   const dim3 grid(static_cast<unsigned>(p.total_tiles)), block(256);
   if (dtype == 1) {
     // the caller built p's work table for bf16_tile(kr_max)
-    if (kr_max <= 32)
+    // short contractions loop over 32-deep chunks (a 64-deep chunk costs a wave per
+    // SIMD in registers: the fused switch at k*r = 64 ran 30% slower with it)
+    if (kr_max <= kLongKR)
       launch_bf16<32, ShortTile>(p, grid, block, s);
-    else if (kr_max <= kLongKR)
-      launch_bf16<64, ShortTile>(p, grid, block, s);
     else
       launch_bf16<64, LongTile>(p, grid, block, s);
   } else {
