@@ -195,7 +195,7 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 #define ADA_WAVES_PER_EU 1
 #endif
 template <int KC, int RB, int CT, int WGN, int RMODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ADA_WAVES_PER_EU, 8)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB >= 4 ? 2 : ADA_WAVES_PER_EU, 8)))
 merge_bf16_kernel(MergeParams p) {
   constexpr int WGM = 4 / WGN;
   constexpr int BM = 16 * RB * WGM, BN = 16 * CT * WGN;
@@ -320,31 +320,36 @@ merge_bf16_kernel(MergeParams p) {
   };
 
   // ---- K-chunk gathers: global -> registers (stage_load), registers -> LDS (stage_store).
-  // Branch-free: out-of-range slots, rows or columns re-read an in-range vector and are
-  // replaced by zeros.  Vector v of a chunk: B row v / (KC/8), k 8 (v % (KC/8));
+  // Branch-free: out-of-range slots, rows or columns re-read an in-range vector, which
+  // is replaced by zeros when stored to LDS (RMODE 3 has no out-of-range slots and
+  // keeps the re-read rows and columns: they only reach outputs that are not stored).
+  // Vector v of a chunk: B row v / (KC/8), k 8 (v % (KC/8));
   // A k row v / (BN/8), columns 8 (v % (BN/8)).  Threads past the vector count (whole
   // waves, as the counts are multiples of 64) skip.
   u32x4 sb[B_VPT];
   float sc[B_VPT];
   u32x4 sa[A_VPT];
+  // Long contractions apply the in-range masks in stage_store: applied at the load,
+  // the AND makes the wave wait for the prefetched chunk before the MFMAs on the
+  // current one.  Short ones (at most one prefetch) mask at the load, which keeps
+  // their registers lower.
+  constexpr bool kDefer = RB >= 4;
+  uint32_t sbm[B_VPT], sam[A_VPT];
 
   // RMODE 3: per-thread parts of the gather offsets, fixed across chunks
   uint32_t b_off3[B_VPT], a_off3[A_VPT];
-  bool b_ok3[B_VPT], a_ok3[A_VPT];
   if constexpr (RMODE == 3) {
 #pragma unroll
     for (int i = 0; i < B_VPT; ++i) {
       const int v = tid + 256 * i;
       const int grow = T.row0 + v / (KC / 8);
-      b_ok3[i] = grow < T.d_out;
-      b_off3[i] = uint32_t(b_ok3[i] ? grow : 0) * uint32_t(r) + 8u * uint32_t(v % (KC / 8));
+      b_off3[i] = uint32_t(grow < T.d_out ? grow : 0) * uint32_t(r) + 8u * uint32_t(v % (KC / 8));
     }
 #pragma unroll
     for (int i = 0; i < A_VPT; ++i) {
       const int v = tid + 256 * i;
       const int gcol = T.col0 + 8 * (v % (BN / 8));
-      a_ok3[i] = gcol < T.d_in;
-      a_off3[i] = uint32_t(v / (BN / 8)) * uint32_t(T.d_in) + uint32_t(a_ok3[i] ? gcol : 0);
+      a_off3[i] = uint32_t(v / (BN / 8)) * uint32_t(T.d_in) + uint32_t(gcol < T.d_in ? gcol : 0);
     }
   }
 
@@ -360,14 +365,14 @@ merge_bf16_kernel(MergeParams p) {
       for (int i = 0; i < B_VPT; ++i) {
         if (NBV % 256 != 0 && tid + 256 * i >= NBV) break;
         const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(bj + b_off3[i]);
-        sb[i] = val & (u32x4)(0u - uint32_t(b_ok3[i]));
+        sb[i] = val;
         sc[i] = c;
       }
 #pragma unroll
       for (int i = 0; i < A_VPT; ++i) {
         if (NAV % 256 != 0 && tid + 256 * i >= NAV) break;
         const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(aj + a_off3[i]);
-        sa[i] = val & (u32x4)(0u - uint32_t(a_ok3[i]));
+        sa[i] = val;
       }
       return;
     }
@@ -388,7 +393,8 @@ merge_bf16_kernel(MergeParams p) {
                   uint32_t(in ? rr : 0)));
         // a mask, not a select: a select of a load lets the compiler sink the load into
         // an exec-masked block of its own
-        sb[i] = val & (u32x4)(0u - uint32_t(in));
+        sbm[i] = 0u - uint32_t(in);
+        sb[i] = kDefer ? val : (val & (u32x4)sbm[i]);
         sc[i] = s_coef[js];
       } else {
         // rank not a multiple of 8: element by element, coefficient applied here
@@ -405,6 +411,7 @@ merge_bf16_kernel(MergeParams p) {
           w[t >> 1] |= hb << (16 * (t & 1));
         }
         sb[i] = (u32x4){w[0], w[1], w[2], w[3]};
+        sbm[i] = ~0u;
         sc[i] = 1.f;
       }
     }
@@ -421,7 +428,8 @@ merge_bf16_kernel(MergeParams p) {
       const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(
           gA + ((uint32_t(s_exp[in ? j : 0]) * uint32_t(r) + uint32_t(in ? rr : 0)) * uint32_t(T.d_in) +
                 uint32_t(in ? gcol : 0)));
-      sa[i] = val & (u32x4)(0u - uint32_t(in));
+      sam[i] = 0u - uint32_t(in);
+      sa[i] = kDefer ? val : (val & (u32x4)sam[i]);
     }
   };
 
@@ -432,10 +440,14 @@ merge_bf16_kernel(MergeParams p) {
       if (NBV % 256 != 0 && v >= NBV) break;
       const int row = v / (KC / 8);
       const int kv = v % (KC / 8);
+      // (RMODE 3 has nothing to mask: an out-of-range row or column re-read row 0 or
+      // column 0, whose products reach only output rows or columns never stored;
+      // short tiles were masked at the load)
+      const u32x4 v8 = (RMODE == 3 || !kDefer) ? sb[i] : (sb[i] & (u32x4)sbm[i]);
       if constexpr (rvec)
-        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = scale_bf16x8(sb[i], sc[i]);
+        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = scale_bf16x8(v8, sc[i]);
       else
-        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = sb[i];
+        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = v8;
     }
 #pragma unroll
     for (int i = 0; i < A_VPT; ++i) {
@@ -443,7 +455,8 @@ merge_bf16_kernel(MergeParams p) {
       if (NAV % 256 != 0 && v >= NAV) break;
       const int kl = v / (BN / 8);
       const int cv = v % (BN / 8);
-      *reinterpret_cast<u32x4*>(&As[buf][kl * LDA + 8 * cv]) = sa[i];
+      *reinterpret_cast<u32x4*>(&As[buf][kl * LDA + 8 * cv]) =
+          (RMODE == 3 || !kDefer) ? sa[i] : (sa[i] & (u32x4)sam[i]);
     }
   };
 
@@ -466,14 +479,8 @@ merge_bf16_kernel(MergeParams p) {
 
   // 4. chunk 0, then the pipelined K loop (one barrier per chunk: chunk c+1 is
   // written to the other buffer, which every wave finished reading at the previous
-  // barrier)
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) stage_load((c + 1) * KC);
+  // barrier).
+  auto mfma_chunk = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < KC / 32; ++ks) {
       bf16x8_t af[CT], bfr[RB];
@@ -495,9 +502,37 @@ merge_bf16_kernel(MergeParams p) {
         for (int ct = 0; ct < CT; ++ct)
           acc[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ct], bfr[rb], acc[rb][ct], 0, 0, 0);
     }
-    if (more) {
+  };
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  if constexpr (kDefer) {
+    // Long contractions: the last chunk is peeled off the loop, so every gather
+    // issued in the loop body is consumed in the same body (a load that could still
+    // be pending at the loop exit would make the compiler wait on it in the
+    // epilogue, and with it on the epilogue's stores), and the gathers are pinned
+    // ahead of the MFMAs (the scheduler would sink them to the end of the chunk to
+    // shorten their live ranges).
+    for (int c = 0; c + 1 < nchunks; ++c) {
+      const int buf = c & 1;
+      stage_load((c + 1) * KC);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk(buf);
+      __builtin_amdgcn_sched_barrier(0);
       stage_store(buf ^ 1);
       __syncthreads();
+    }
+    mfma_chunk((nchunks - 1) & 1);
+  } else {
+    for (int c = 0; c < nchunks; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < nchunks;
+      if (more) stage_load((c + 1) * KC);
+      mfma_chunk(buf);
+      if (more) {
+        stage_store(buf ^ 1);
+        __syncthreads();
+      }
     }
   }
 
