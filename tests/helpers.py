@@ -8,8 +8,12 @@ from oracle import adafuse as O
 from weight_merge_amd import synth
 
 # Merged bf16 weights: |W'_gpu - W'_ref| <= 8e-3 |W'_ref| + 1e-4, ref the unrounded
-# fp64 W + delta.  bf16 round-to-nearest alone costs <= 2^-8 |W'| (about half the
-# relative term); folding s*g into B in bf16 adds <= 2^-8 |delta| ~ 1e-6 absolute.
+# fp64 W + delta.  The kernel's arithmetic is RNE(W + sum_t RNE(s g b_t) a_t) with exact
+# products and fp32 sums, so its error is at most 2^-9 |W'| (final rounding) plus
+# 2^-9 sum_t |s g b_t a_t| (gate folded into B in bf16) plus the fp32 accumulation.
+# The second term is far below 1e-4 on weight-shaped data (d_in in the thousands, so
+# A ~ N(0, 1/sqrt(d_in)) is small); folded_bound() states the full bound for inputs
+# where it is not.
 BF16_RTOL, BF16_ATOL = 8e-3, 1e-4
 # fp32 storage: one final rounding (2^-24 relative) plus fp32 accumulation over k*r
 # terms; 1e-6 relative + 1e-7 absolute leaves a >10x margin and still catches a
@@ -38,6 +42,18 @@ def check_close(got: torch.Tensor | np.ndarray, ref: np.ndarray, rtol: float, at
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; worst at {i}: "
                              f"got {g[i]!r} ref {ref[i]!r} err {err[i]:.3e} bound {bound[i]:.3e}")
     return float(np.max(err / (np.abs(ref) + atol / rtol))) if err.size else 0.0
+
+
+def folded_bound(Aw, Bw, idx, gate, scale: float) -> np.ndarray:
+    """Per-element error bound of the bf16 merge's arithmetic beyond the stated
+    tolerance: 2^-8 sum_t |s g b_t a_t| over the selected adapters (twice the worst
+    case of rounding s g B to bf16, for margin)."""
+    A64, B64 = to64(Aw), to64(Bw)
+    acc = np.zeros((B64.shape[1], A64.shape[2]))
+    for e, g in zip(np.asarray(idx).tolist(), np.asarray(gate, dtype=np.float64).tolist()):
+        if 0 <= e < A64.shape[0] and g != 0.0:
+            acc += np.abs(scale * g * B64[e]) @ np.abs(A64[e])
+    return 2.0 ** -8 * acc
 
 
 def min_gap(z) -> float:

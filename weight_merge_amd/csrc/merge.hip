@@ -54,6 +54,17 @@ __device__ __forceinline__ ADA_GLOBAL T* as_global_mut(void* p) {
 }
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte access at a uniform base plus a 32-bit per-lane byte offset: the form the
+// compiler maps onto global_load/store with a scalar base and a 32-bit vector offset,
+// with no 64-bit address arithmetic per access.  Every W matrix and adapter bank has
+// fewer than 2^31 elements, so byte offsets fit in 32 bits.
+__device__ __forceinline__ u32x4 load16(const ADA_GLOBAL unsigned char* base, uint32_t off) {
+  return *reinterpret_cast<const ADA_GLOBAL u32x4*>(base + off);
+}
+__device__ __forceinline__ void store16(ADA_GLOBAL unsigned char* base, uint32_t off, u32x4 v) {
+  *reinterpret_cast<ADA_GLOBAL u32x4*>(base + off) = v;
+}
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -235,10 +246,11 @@ merge_bf16_kernel(MergeParams p) {
   const int wy = wave / WGN, wx = wave % WGN;
 
   const TileRef T = find_tile(p, BM, BN);
-  const ADA_GLOBAL uint16_t* __restrict__ src = as_global<uint16_t>(T.src);
-  ADA_GLOBAL uint16_t* __restrict__ dst = as_global_mut<uint16_t>(T.dst);
-  const ADA_GLOBAL uint16_t* __restrict__ gA = as_global<uint16_t>(T.a);
-  const ADA_GLOBAL uint16_t* __restrict__ gB = as_global<uint16_t>(T.b);
+  const ADA_GLOBAL unsigned char* __restrict__ src = as_global<unsigned char>(T.src);
+  ADA_GLOBAL unsigned char* __restrict__ dst = as_global_mut<unsigned char>(T.dst);
+  const ADA_GLOBAL unsigned char* __restrict__ gA = as_global<unsigned char>(T.a);
+  const ADA_GLOBAL unsigned char* __restrict__ gB = as_global<unsigned char>(T.b);
+  const ADA_GLOBAL uint16_t* __restrict__ gB16 = as_global<uint16_t>(T.b);
 
   // 1. selection (wave 0): lane j holds slot j of each selection (branch-free: lanes
   // past k re-read slot 0, which always exists, and are discarded below; exec-masked
@@ -261,7 +273,7 @@ merge_bf16_kernel(MergeParams p) {
   //    which streams about 20% slower)
   constexpr int NV = BM * BN / 8 / 256;
   static_assert(NV * 2048 == BM * BN, "W split");
-  uint32_t woff[NV];  // element offsets: every W matrix has fewer than 2^31 elements
+  uint32_t woff[NV];  // byte offsets
   bool ok[NV];
   u32x4 wv[NV];
 #pragma unroll
@@ -270,8 +282,8 @@ merge_bf16_kernel(MergeParams p) {
     const int row = T.row0 + v / (BN / 8);
     const int col = T.col0 + 8 * (v % (BN / 8));
     ok[u] = row < T.d_out && col < T.d_in;
-    woff[u] = ok[u] ? uint32_t(row) * uint32_t(T.ld) + uint32_t(col) : 0u;  // out of range: re-read W[0][0..8)
-    wv[u] = *reinterpret_cast<const ADA_GLOBAL u32x4*>(src + woff[u]);
+    woff[u] = ok[u] ? 2u * (uint32_t(row) * uint32_t(T.ld) + uint32_t(col)) : 0u;  // out of range: re-read W[0][0..8)
+    wv[u] = load16(src, woff[u]);
   }
 
   // 3. active slots, in selection order: index in range and coefficient nonzero
@@ -299,7 +311,7 @@ merge_bf16_kernel(MergeParams p) {
     if (T.src == T.dst) return;
 #pragma unroll
     for (int u = 0; u < NV; ++u)
-      if (ok[u]) *reinterpret_cast<ADA_GLOBAL u32x4*>(dst + woff[u]) = wv[u];
+      if (ok[u]) store16(dst, woff[u], wv[u]);
     return;
   }
 
@@ -343,13 +355,13 @@ merge_bf16_kernel(MergeParams p) {
     for (int i = 0; i < B_VPT; ++i) {
       const int v = tid + 256 * i;
       const int grow = T.row0 + v / (KC / 8);
-      b_off3[i] = uint32_t(grow < T.d_out ? grow : 0) * uint32_t(r) + 8u * uint32_t(v % (KC / 8));
+      b_off3[i] = 2u * (uint32_t(grow < T.d_out ? grow : 0) * uint32_t(r) + 8u * uint32_t(v % (KC / 8)));
     }
 #pragma unroll
     for (int i = 0; i < A_VPT; ++i) {
       const int v = tid + 256 * i;
       const int gcol = T.col0 + 8 * (v % (BN / 8));
-      a_off3[i] = uint32_t(v / (BN / 8)) * uint32_t(T.d_in) + uint32_t(gcol < T.d_in ? gcol : 0);
+      a_off3[i] = 2u * (uint32_t(v / (BN / 8)) * uint32_t(T.d_in) + uint32_t(gcol < T.d_in ? gcol : 0));
     }
   }
 
@@ -359,19 +371,19 @@ merge_bf16_kernel(MergeParams p) {
       const int rr0 = k0 & (r - 1);
       const int e = __builtin_amdgcn_readfirstlane(s_exp[j]);
       const float c = s_coef[j];
-      const ADA_GLOBAL uint16_t* bj = gB + uint32_t(e) * uint32_t(T.d_out) * uint32_t(r) + uint32_t(rr0);
-      const ADA_GLOBAL uint16_t* aj = gA + (uint32_t(e) * uint32_t(r) + uint32_t(rr0)) * uint32_t(T.d_in);
+      const ADA_GLOBAL unsigned char* bj = gB + 2u * (uint32_t(e) * uint32_t(T.d_out) * uint32_t(r) + uint32_t(rr0));
+      const ADA_GLOBAL unsigned char* aj = gA + 2u * ((uint32_t(e) * uint32_t(r) + uint32_t(rr0)) * uint32_t(T.d_in));
 #pragma unroll
       for (int i = 0; i < B_VPT; ++i) {
         if (NBV % 256 != 0 && tid + 256 * i >= NBV) break;
-        const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(bj + b_off3[i]);
+        const u32x4 val = load16(bj, b_off3[i]);
         sb[i] = val;
         sc[i] = c;
       }
 #pragma unroll
       for (int i = 0; i < A_VPT; ++i) {
         if (NAV % 256 != 0 && tid + 256 * i >= NAV) break;
-        const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(aj + a_off3[i]);
+        const u32x4 val = load16(aj, a_off3[i]);
         sa[i] = val;
       }
       return;
@@ -388,9 +400,9 @@ merge_bf16_kernel(MergeParams p) {
         split(k0 + 8 * kv, j, rr);
         const bool in = j < nslot && grow < T.d_out;
         const int js = in ? j : 0;
-        const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(
-            gB + ((uint32_t(s_exp[js]) * uint32_t(T.d_out) + uint32_t(in ? grow : 0)) * uint32_t(r) +
-                  uint32_t(in ? rr : 0)));
+        const u32x4 val = load16(
+            gB, 2u * ((uint32_t(s_exp[js]) * uint32_t(T.d_out) + uint32_t(in ? grow : 0)) * uint32_t(r) +
+                      uint32_t(in ? rr : 0)));
         // a mask, not a select: a select of a load lets the compiler sink the load into
         // an exec-masked block of its own
         sbm[i] = 0u - uint32_t(in);
@@ -405,7 +417,7 @@ merge_bf16_kernel(MergeParams p) {
           split(k0 + 8 * kv + t, j, rr);
           float x = 0.f;
           if (j < nslot && grow < T.d_out)
-            x = __uint_as_float(uint32_t(gB[(int64_t(s_exp[j]) * T.d_out + grow) * r + rr]) << 16) *
+            x = __uint_as_float(uint32_t(gB16[(int64_t(s_exp[j]) * T.d_out + grow) * r + rr]) << 16) *
                 s_coef[j];
           const uint32_t hb = pack_bf16x2(x, 0.f) & 0xffffu;
           w[t >> 1] |= hb << (16 * (t & 1));
@@ -425,9 +437,9 @@ merge_bf16_kernel(MergeParams p) {
       split(k0 + kl, j, rr);
       const int gcol = T.col0 + 8 * cv;
       const bool in = j < nslot && gcol < T.d_in;
-      const u32x4 val = *reinterpret_cast<const ADA_GLOBAL u32x4*>(
-          gA + ((uint32_t(s_exp[in ? j : 0]) * uint32_t(r) + uint32_t(in ? rr : 0)) * uint32_t(T.d_in) +
-                uint32_t(in ? gcol : 0)));
+      const u32x4 val = load16(
+          gA, 2u * ((uint32_t(s_exp[in ? j : 0]) * uint32_t(r) + uint32_t(in ? rr : 0)) * uint32_t(T.d_in) +
+                    uint32_t(in ? gcol : 0)));
       sam[i] = 0u - uint32_t(in);
       sa[i] = kDefer ? val : (val & (u32x4)sam[i]);
     }
@@ -562,7 +574,7 @@ merge_bf16_kernel(MergeParams p) {
     o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
     o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
     o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
-    *reinterpret_cast<ADA_GLOBAL u32x4*>(dst + woff[u]) = o;
+    store16(dst, woff[u], o);
   }
 }
 
