@@ -202,11 +202,13 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 //   2: any other r (division; B element by element)
 //   3: r a power of two and a multiple of KC: every chunk lies inside one slot, so the
 //      slot, its coefficient and its base addresses are uniform per chunk
+// LONG marks the long-contraction instantiation (k*r > 64: 128 x 128 tiles, 64-deep
+// chunks): it asks for two waves per SIMD and defers the gather masks (step 4).
 #ifndef ADA_WAVES_PER_EU
 #define ADA_WAVES_PER_EU 1
 #endif
-template <int KC, int RB, int CT, int WGN, int RMODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB >= 4 ? 2 : ADA_WAVES_PER_EU, 8)))
+template <int KC, int RB, int CT, int WGN, int RMODE, bool LONG>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LONG ? 2 : ADA_WAVES_PER_EU, 8)))
 merge_bf16_kernel(MergeParams p) {
   constexpr int WGM = 4 / WGN;
   constexpr int BM = 16 * RB * WGM, BN = 16 * CT * WGN;
@@ -215,7 +217,7 @@ merge_bf16_kernel(MergeParams p) {
   // transposed read (4 k rows x 4 column chunks) touch 16 disjoint bank pairs; the
   // short-contraction tiles read A once per tile and keep the smaller pitch, whose
   // LDS footprint stays under the delta tile's
-  constexpr int LDA = BN + (RB >= 4 ? 32 : 8);
+  constexpr int LDA = BN + (LONG ? 32 : 8);
   constexpr int NBV = BM * KC / 8;  // 16-byte B vectors per chunk
   constexpr int NAV = KC * BN / 8;  // 16-byte A vectors per chunk
   constexpr int B_VPT = (NBV + 255) / 256;
@@ -345,7 +347,7 @@ merge_bf16_kernel(MergeParams p) {
   // the AND makes the wave wait for the prefetched chunk before the MFMAs on the
   // current one.  Short ones (at most one prefetch) mask at the load, which keeps
   // their registers lower.
-  constexpr bool kDefer = RB >= 4;
+  constexpr bool kDefer = LONG;
   uint32_t sbm[B_VPT], sam[A_VPT];
 
   // RMODE 3: per-thread parts of the gather offsets, fixed across chunks
@@ -664,16 +666,16 @@ __global__ void __launch_bounds__(256) merge_f32_kernel(MergeParams p) {
   }
 }
 
-template <int KC, class S>
+template <int KC, class S, bool LONG>
 void launch_bf16(const MergeParams& p, dim3 grid, dim3 block, hipStream_t s) {
   if (p.r_shift >= 0 && p.r % KC == 0)
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 3>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 3, LONG>), grid, block, 0, s, p);
   else if (p.r_shift >= 0 && (p.r & 7) == 0)
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 0>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 0, LONG>), grid, block, 0, s, p);
   else if ((p.r & 7) == 0)
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 1>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 1, LONG>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 2>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 2, LONG>), grid, block, 0, s, p);
 }
 
 }  // namespace
@@ -686,9 +688,9 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t
     // short contractions loop over 32-deep chunks (a 64-deep chunk costs a wave per
     // SIMD in registers: the fused switch at k*r = 64 ran 30% slower with it)
     if (kr_max <= kLongKR)
-      launch_bf16<32, ShortTile>(p, grid, block, s);
+      launch_bf16<32, ShortTile, false>(p, grid, block, s);
     else
-      launch_bf16<64, LongTile>(p, grid, block, s);
+      launch_bf16<64, LongTile, true>(p, grid, block, s);
   } else {
     hipLaunchKernelGGL(merge_f32_kernel<32>, grid, block, 0, s, p);
   }
