@@ -18,7 +18,7 @@
  *   - Every tensor pointer is a DEVICE pointer unless stated otherwise, 16-byte
  *     aligned, row-major, owned by the caller.  The library never allocates or
  *     frees caller memory, and the hot calls (pregate, merge, unmerge, switch,
- *     decode_gemv, lora_apply) allocate nothing at all.
+ *     decode_gemv, lora_apply, lora_layer) allocate nothing at all.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *     calls are asynchronous on that stream and return once the work is enqueued.
  *   - Return value: ADA_OK (0) or a negative ada_status.  All argument checks run
@@ -175,7 +175,8 @@ typedef struct {
  * every expand.  This is the strongest unmerged comparator for the merged path
  * ([pt] technical summary 1: several kernel calls per layer in the conventional
  * design).  All projections share E, r, the selection and the dtype.  `workspace`:
- * caller-owned device memory of at least sum_p (d_out_p + k*r) * 4 bytes.
+ * caller-owned device memory of at least 4 * sum_p roundup4(d_out_p + k*r) bytes
+ * (one fp32 block per projection, each starting 16-byte aligned).
  */
 int ada_lora_layer(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_t r,
                    const int32_t* idx, const float* gate, int32_t k, float scale,
