@@ -276,6 +276,42 @@ def run_e2e(args, cfg, torch, A, synth, dev):
     del g_backbone, g_merged, g_base, g_fused
     simple = simple_fusion_ms(torch, st, cfg, idx, gate, 3)
 
+    # N4: a batch of requests, each pre-gated once on its own leading token (so each has
+    # its own selection), decoding together: a merged backbone holds one selection, so
+    # the batch runs the unmerged path, every W row read once per step for all requests
+    batch = {}
+    for nb in (4, 8, 16):
+        bidx = torch.empty(nb, cfg.k, dtype=torch.int32, device=dev)
+        bgate = torch.empty(nb, cfg.k, dtype=torch.float32, device=dev)
+        for b in range(nb):
+            hb, _ = synth.router_inputs(cfg, args.seed + 100 + b)
+            A.ada_pregate(hb.to(dev), R, cfg.k, cfg.renorm, bidx[b], bgate[b])
+        xb = synth.decode_inputs(cfg, args.seed + 1, nb, device=dev)
+        yb = [[torch.empty(nb, proj.d_out, dtype=torch.bfloat16, device=dev) for proj in cfg.projections]
+              for _ in range(cfg.n_layers)]
+        bws = [torch.empty(A.lora_batch_workspace_elems([p.d_out for p in cfg.projections], nb, cfg.k, cfg.r),
+                           dtype=torch.float32, device=dev) for _ in range(cfg.n_layers)]
+
+        def token_batch():
+            for l in range(cfg.n_layers):
+                A.ada_lora_batch([(st.W[l][p], st.A[l][p], st.B[l][p], xb[proj.name], yb[l][p])
+                                  for p, proj in enumerate(cfg.projections)], bidx, bgate, cfg.scale, bws[l])
+
+        g_batch = graph_of(token_batch)
+        t_batch = time_ms(torch, g_batch.replay, reps)
+        del g_batch
+        torch.cuda.synchronize()
+        batch[str(nb)] = {
+            "distinct_selections": len({tuple(row) for row in bidx.cpu().tolist()}),
+            "step_graph_ms": round(t_batch, 4),
+            "tokens_per_s": round(nb / t_batch * 1e3, 1),
+            "vs_batch1_merged_tokens_per_s": round(nb * merged_graph / t_batch, 3),
+            # derived, not timed: serving the same requests one at a time on merged
+            # weights, switching the selection before each request's token
+            "serial_switching_step_ms_derived": round(nb * (t_switch + merged_graph), 3),
+        }
+        del yb, bws, xb
+
     launches_merged = cfg.n_layers * len(cfg.projections)
     launches_base = cfg.n_layers * (1 + 3 * len(cfg.projections))
     req_graph = t_pregate + pair + steps * merged_graph
@@ -324,6 +360,7 @@ def run_e2e(args, cfg, torch, A, synth, dev):
         "speedup_request_graph": round(req_base_graph / req_graph, 3),
         "speedup_request_eager": round(req_base_eager / req_eager, 3),
         "overhead_vs_backbone_graph": round(merged_graph / backbone_graph - 1, 4),
+        "batch_mixed_selections_unmerged": batch,
     }
     print(json.dumps(out), flush=True)
 

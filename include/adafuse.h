@@ -18,7 +18,7 @@
  *   - Every tensor pointer is a DEVICE pointer unless stated otherwise, 16-byte
  *     aligned, row-major, owned by the caller.  The library never allocates or
  *     frees caller memory, and the hot calls (pregate, merge, unmerge, switch,
- *     decode_gemv, lora_apply, lora_layer) allocate nothing at all.
+ *     decode_gemv, lora_apply, lora_layer, lora_batch) allocate nothing at all.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *     calls are asynchronous on that stream and return once the work is enqueued.
  *   - Return value: ADA_OK (0) or a negative ada_status.  All argument checks run
@@ -179,6 +179,23 @@ typedef struct {
  * (one fp32 block per projection, each starting 16-byte aligned).
  */
 int ada_lora_layer(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_t r,
+                   const int32_t* idx, const float* gate, int32_t k, float scale,
+                   void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream);
+
+/*
+ * A batch of nb requests (1 <= nb <= 16), each with its OWN selection, through one
+ * layer of the unmerged routed path, in two launches.  The pages treat batch-1
+ * requests with one selection each; a merged backbone can hold only one selection,
+ * so requests with different selections are served unmerged:
+ *   y_b = RNE(w @ x_b + scale * sum_j gate[b][j] * B[idx[b][j]] (A[idx[b][j]] x_b)).
+ * Every W row is read once for the whole batch (the base product runs on MFMA, 16
+ * rows by 16 requests per wave).  Per projection, x is [nb][d_in] and y is
+ * [nb][d_out] (rows contiguous); idx and gate are device arrays [nb][k].  Request
+ * b's result equals ada_lora_layer on (x_b, idx[b], gate[b]) up to the order of the
+ * base product's fp32 sums.  `workspace`: caller-owned device memory of at least
+ * 4 * sum_p roundup4(nb * (d_out_p + k*r)) bytes.
+ */
+int ada_lora_batch(const ada_lora_proj* projs, int32_t n_proj, int32_t nb, int32_t E, int32_t r,
                    const int32_t* idx, const float* gate, int32_t k, float scale,
                    void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream);
 

@@ -178,3 +178,28 @@ def test_lora_layer_validation(lib):
     assert f(arr(d_in=60), 1, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
     assert f(arr(), 1, 4, 8, P, P2, 2, 2.0, P, ws - 16, ADA_BF16, None) == ADA_ESHAPE
     assert f(arr(), 1, 4, 8, P, P2, 2, 2.0, MIS, ws, ADA_BF16, None) == ADA_EALIGN
+
+
+def test_lora_batch_validation(lib):
+    from weight_merge_amd._lib import AdaLoraProj
+    good = dict(w=P, a=P2, b=P, x=P2, y=P, d_out=64, d_in=64, ld_w=64)
+
+    def arr(**kw):
+        a = dict(good, **kw)
+        return (AdaLoraProj * 1)(AdaLoraProj(a["w"], a["a"], a["b"], a["x"], a["y"], a["d_out"], a["d_in"], a["ld_w"]))
+
+    f = lib.ada_lora_batch
+    nb = 3
+    ws = nb * (64 + 2 * 8) * 4  # exactly what one 64-row projection with k*r = 16 needs for 3 requests
+    assert f(None, 1, nb, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(), 1, nb, 4, 8, None, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(), 1, nb, 4, 8, P, P2, 2, 2.0, None, ws, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(), 1, nb, 4, 8, P, P2, 2, 2.0, P, ws, 5, None) == ADA_EDTYPE
+    assert f(arr(), 1, 0, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 1, 17, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 17, nb, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 1, nb, 4, 8, P, P2, 5, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(d_out=60), 1, nb, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(x=MIS), 1, nb, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EALIGN
+    assert f(arr(), 1, nb, 4, 8, P, P2, 2, 2.0, P, ws - 16, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(), 1, nb, 4, 8, P, P2, 2, 2.0, MIS, ws, ADA_BF16, None) == ADA_EALIGN

@@ -442,3 +442,48 @@ def test_lora_layer_matches_oracle_and_the_three_launch_path(dt, E, r, k):
         mag = np.abs(W64) @ np.abs(x64)
         err = np.abs(to64(y) - ref)
         assert np.all(err <= gemv_bound(W64, x64, ref, dt) + 1e-4 * mag), float(err.max())
+
+
+# ---------------------------------------------------------------- batch, mixed selections
+
+
+@pytest.mark.parametrize("dt,E,r,k,nb", [("bf16", 8, 16, 2, 1), ("bf16", 8, 16, 2, 3), ("bf16", 16, 64, 4, 8),
+                                         ("bf16", 8, 16, 2, 16), ("fp32", 4, 8, 2, 5)])
+def test_lora_batch_serves_a_selection_per_request(dt, E, r, k, nb):
+    """A batch of requests with different selections through one layer: request b is
+    within the GEMV bound of the oracle's routed forward with that request's selection,
+    and agrees with the single-request layer path on (x_b, idx_b, gate_b) to rounding
+    (the batched base product sums on MFMA, in another order).  One request carries an
+    out-of-range index and a zero gate, both skipped."""
+    shapes = [(264, 520), (1032, 264), (8, 8), (136, 136)]
+    sels = [make_selection(E, k, 64, dt, 40 + 7 * b) for b in range(nb)]
+    idx = torch.stack([s[0] for s in sels]).contiguous()
+    gate = torch.stack([s[1] for s in sels]).contiguous()
+    if nb > 1:
+        idx[1, 0] = E + 3
+        gate[1, k - 1] = 0.0
+        assert len({tuple(row) for row in idx.tolist()}) > 1, "the batch must mix selections"
+    banks = [synth.adapter_bank(400 + i, E, r, do, di, dt) for i, (do, di) in enumerate(shapes)]
+    xs = [synth.host_normal(synth.tensor_seed(500 + i, di), (nb, di), 1.0, dt) for i, (_, di) in enumerate(shapes)]
+    dev = [(W.to(DEV), Aw.to(DEV), Bw.to(DEV), x.to(DEV)) for (W, Aw, Bw), x in zip(banks, xs)]
+    ys = [torch.full((nb, W.shape[0]), float("nan"), dtype=TD[dt], device=DEV) for W, _, _ in banks]
+    didx, dgate = idx.to(DEV), gate.to(DEV)
+    A.ada_lora_batch([(w, a, b, x, y) for (w, a, b, x), y in zip(dev, ys)], didx, dgate, 2.0)
+    singles = []
+    for bq in range(nb):
+        y1 = [torch.full((W.shape[0],), float("nan"), dtype=TD[dt], device=DEV) for W, _, _ in banks]
+        A.ada_lora_layer([(w, a, b, x[bq].contiguous(), y) for (w, a, b, x), y in zip(dev, y1)],
+                         didx[bq].contiguous(), dgate[bq].contiguous(), 2.0)
+        singles.append(y1)
+    sync()
+    for bq in range(nb):
+        keep = [(e, g) for e, g in zip(idx[bq].tolist(), gate[bq].tolist()) if 0 <= e < E]
+        for pi, ((W, Aw, Bw), x) in enumerate(zip(banks, xs)):
+            got = ys[pi][bq].cpu()
+            W64, x64 = to64(W), to64(x[bq])
+            one = to64(singles[bq][pi])
+            assert np.all(np.abs(to64(got) - one) <= gemv_bound(W64, x64, one, dt)), (bq, pi)
+            ref = O.routed_lora_forward(to64(W), to64(Aw), to64(Bw), [e for e, _ in keep],
+                                        np.array([g for _, g in keep], dtype=np.float64), 2.0, to64(x[bq]))
+            err = np.abs(to64(got) - ref)
+            assert np.all(err <= gemv_bound(W64, x64, ref, dt) + 1e-4 * (np.abs(W64) @ np.abs(x64))), (bq, pi)

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     AdaModel,
     ada_decode_gemv,
     ada_lora_apply,
+    ada_lora_batch,
     ada_lora_layer,
     ada_merge,
     ada_pregate,

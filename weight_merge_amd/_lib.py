@@ -59,6 +59,8 @@ _SIGNATURES = {
                                       c_void_p, c_int64, c_int32, c_void_p]),
     "ada_lora_layer": (ctypes.c_int, [ctypes.POINTER(AdaLoraProj), c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                       c_int32, c_float, c_void_p, c_int64, c_int32, c_void_p]),
+    "ada_lora_batch": (ctypes.c_int, [ctypes.POINTER(AdaLoraProj), c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                      c_void_p, c_int32, c_float, c_void_p, c_int64, c_int32, c_void_p]),
 }
 
 _lib = None

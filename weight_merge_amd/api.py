@@ -232,3 +232,47 @@ def ada_lora_layer(projs, idx, gate, scale: float, workspace=None, stream=None):
     st = _lib.load().ada_lora_layer(arr, len(projs), E, r, pi, pg, k, float(scale), _dev(workspace, "workspace"),
                                     workspace.numel() * workspace.element_size(), _dtype(w0), _stream(stream))
     _check(st, "ada_lora_layer")
+
+
+def lora_batch_workspace_elems(d_outs, nb: int, k: int, r: int) -> int:
+    """fp32 elements of workspace ada_lora_batch needs for these projections."""
+    n = 0
+    for d in d_outs:
+        n = (n + nb * (d + k * r) + 3) // 4 * 4
+    return n
+
+
+def ada_lora_batch(projs, idx, gate, scale: float, workspace=None, stream=None):
+    """One layer of the unmerged routed path for a batch of requests with a selection
+    each (two launches for all projections and requests).
+
+    projs: list of (w, a, b, x, y) with w [d_out, d_in], a [E, r, d_in], b [E, d_out, r],
+    x [nb, d_in], y [nb, d_out] (written); idx int32 [nb, k], gate fp32 [nb, k]."""
+    projs = list(projs)
+    w0, a0 = projs[0][0], projs[0][1]
+    E, r, _ = a0.shape
+    if idx.dim() != 2 or idx.shape != gate.shape:
+        raise ValueError("idx and gate must be [nb, k] and of equal shape")
+    if idx.dtype != torch.int32 or gate.dtype != torch.float32:
+        raise TypeError("idx must be int32 and gate float32")
+    _contig(idx, "idx")
+    _contig(gate, "gate")
+    nb, k = idx.shape
+    arr = (AdaLoraProj * len(projs))()
+    for i, (w, a, b, x, y) in enumerate(projs):
+        d_out, d_in = w.shape
+        if w.stride(1) != 1:
+            raise ValueError("w must have unit column stride")
+        for t, n in ((a, "a"), (b, "b"), (x, "x"), (y, "y")):
+            _contig(t, n)
+        if a.shape != (E, r, d_in) or b.shape != (E, d_out, r) or x.shape != (nb, d_in) or y.shape != (nb, d_out):
+            raise ValueError("projection shapes do not match")
+        arr[i] = AdaLoraProj(_dev(w, "w"), _dev(a, "a"), _dev(b, "b"), _dev(x, "x"), _dev(y, "y"), d_out, d_in,
+                             w.stride(0))
+    need = lora_batch_workspace_elems([p[0].shape[0] for p in projs], nb, k, r)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.float32, device=w0.device)
+    st = _lib.load().ada_lora_batch(arr, len(projs), nb, E, r, _dev(idx, "idx"), _dev(gate, "gate"), k,
+                                    float(scale), _dev(workspace, "workspace"),
+                                    workspace.numel() * workspace.element_size(), _dtype(w0), _stream(stream))
+    _check(st, "ada_lora_batch")

@@ -109,11 +109,20 @@ struct LoraLayerParams {
   int32_t E;
   int32_t r;
   int32_t k;
-  const int32_t* idx;
-  const float* gate;
+  const int32_t* idx;  // [nb][k]
+  const float* gate;   // [nb][k]
   float scale;
   float* ws;
+  int32_t nb;          // requests of a batch (ada_lora_batch); 1 for ada_lora_layer
 };
 hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s);
+
+// A batch of requests with a selection each, one layer (the unmerged path serving mixed
+// selections).  Per projection x is [nb][d_in], y [nb][d_out]; dot_row0 counts waves of
+// the first grid: ceil(d_out / 16) base waves (16 W rows for every request) then
+// nb * k*r shrink rows; out_row0 indexes the nb * d_out outputs; ws_off is an fp32
+// block of nb * (d_out + k*r).
+constexpr int kMaxBatch = 16;
+hipError_t launch_lora_batch(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s);
 
 }  // namespace ada

@@ -190,6 +190,116 @@ __global__ void __launch_bounds__(256) lora_layer_expand_kernel(LoraLayerParams 
                        ws + P.d_out));
 }
 
+// ---- a batch of requests, each with its own selection (one layer, two launches).
+// Grid 1, in units of waves: per projection, ceil(d_out/16) waves for the base product
+// and nb*k*r waves for the shrink rows.  A base wave computes Y[16 rows][16 requests]
+// = W[rows] X^T on MFMA (v_mfma_f32_16x16x32_bf16; fp32: 16x16x4), so each W row is
+// read from HBM once for the whole batch and each request's activations once per 16
+// rows.  Lane l = 16 q + i supplies W[row i][k .. k+7] and X[request i][k .. k+7]
+// (k = k0 + 8 q) and receives D[4 q + c][i] = sum_k W[row 4q + c][k] X[request i][k].
+// Rows past d_out and requests past nb re-read row / request 0 and are not stored.
+// Grid 2: every request's expand (as ada_lora_layer).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ f32x4 base_tile(const T* __restrict__ W, int64_t ld, int row0, int d_out,
+                                           const T* __restrict__ X, int d_in, int nb) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, i = lane & 15;
+  const T* wrow = W + int64_t(row0 + i < d_out ? row0 + i : 0) * ld;
+  const T* xrow = X + int64_t(i < nb ? i : 0) * d_in;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 2) {
+    constexpr int U = 4;  // 32-deep steps in flight
+    for (int k0 = 0; k0 < d_in; k0 += 32 * U) {
+      uint4 wv[U], xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + 32 * u + 8 * q;
+        const bool in = k < d_in;  // d_in is a multiple of 8: whole vectors in or out
+        const uint4 w = *reinterpret_cast<const uint4*>(wrow + (in ? k : 0));
+        const uint4 x = *reinterpret_cast<const uint4*>(xrow + (in ? k : 0));
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        wv[u] = in ? w : z;
+        xv[u] = in ? x : z;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[u]),
+                                                      __builtin_bit_cast(bf16x8_t, xv[u]), acc, 0, 0, 0);
+    }
+  } else {
+    // fp32: lane (q, i) loads 4 consecutive k; MFMA j takes element j of every lane,
+    // i.e. k = k0 + 4 q + j (the same permutation of k on both operands)
+    for (int k0 = 0; k0 < d_in; k0 += 16) {
+      const int k = k0 + 4 * q;
+      const bool in = k < d_in;  // d_in is a multiple of 8: whole 4-vectors in or out
+      const float4 w = *reinterpret_cast<const float4*>(wrow + (in ? k : 0));
+      const float4 x = *reinterpret_cast<const float4*>(xrow + (in ? k : 0));
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 wm = in ? w : z, xm = in ? x : z;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wm.x, xm.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wm.y, xm.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wm.z, xm.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wm.w, xm.w, acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) lora_batch_dot_kernel(LoraLayerParams p) {
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave index
+  int q = 0;
+  while (q < p.n - 1 && g >= p.proj[q + 1].dot_row0) ++q;
+  const LoraLayerProj& P = p.proj[q];
+  const int lw = g - P.dot_row0;
+  const int kr = p.k * p.r;
+  const int base_waves = (P.d_out + 15) / 16;
+  if (lw >= base_waves + p.nb * kr) return;
+  const T* x = static_cast<const T*>(P.x);
+  float* ws = p.ws + P.ws_off;
+  if (lw < base_waves) {
+    const int row0 = 16 * lw;
+    const f32x4 acc = base_tile(static_cast<const T*>(P.w), P.ld, row0, P.d_out, x, P.d_in, p.nb);
+    const int i = lane & 15, qq = lane >> 4;
+    if (i < p.nb) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int row = row0 + 4 * qq + c;
+        if (row < P.d_out) ws[int64_t(i) * P.d_out + row] = acc[c];
+      }
+    }
+  } else {
+    const int sr = lw - base_waves;  // request b, slot j, rank rr
+    const int b = sr / kr, rem = sr - b * kr, j = rem / p.r, rr = rem - j * p.r;
+    const int e = p.idx[b * p.k + j];
+    float s = 0.f;
+    if (e >= 0 && e < p.E)
+      s = row_dot<T, kGemvBatch>(static_cast<const T*>(P.a) + (int64_t(e) * p.r + rr) * P.d_in,
+                                 x + int64_t(b) * P.d_in, P.d_in);
+    if (lane == 0) ws[int64_t(p.nb) * P.d_out + sr] = s;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) lora_batch_expand_kernel(LoraLayerParams p) {
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  int q = 0;
+  while (q < p.n - 1 && g >= p.proj[q + 1].out_row0) ++q;
+  const LoraLayerProj& P = p.proj[q];
+  const int o = g - P.out_row0;
+  if (o >= p.nb * P.d_out) return;
+  const int b = o / P.d_out, i = o - b * P.d_out;
+  const int kr = p.k * p.r;
+  const float* ws = p.ws + P.ws_off;
+  store_out(static_cast<T*>(P.y), o,
+            expand_row(static_cast<const T*>(P.b), p.E, p.r, P.d_out, i, p.idx + b * p.k, p.gate + b * p.k, p.k,
+                       p.scale, ws[o], ws + int64_t(p.nb) * P.d_out + int64_t(b) * kr));
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const void* w, int d_out, int d_in, int64_t ld, const void* x, void* y,
@@ -237,6 +347,18 @@ hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_row
   } else {
     hipLaunchKernelGGL(lora_layer_dot_kernel<float>, g1, block, 0, s, p);
     hipLaunchKernelGGL(lora_layer_expand_kernel<float>, g2, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_batch(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s) {
+  const dim3 g1((dot_rows + 3) / 4), g2((out_rows + 255) / 256), block(256);
+  if (dtype == 1) {
+    hipLaunchKernelGGL(lora_batch_dot_kernel<uint16_t>, g1, block, 0, s, p);
+    hipLaunchKernelGGL(lora_batch_expand_kernel<uint16_t>, g2, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL(lora_batch_dot_kernel<float>, g1, block, 0, s, p);
+    hipLaunchKernelGGL(lora_batch_expand_kernel<float>, g2, block, 0, s, p);
   }
   return hipGetLastError();
 }
