@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--cpu-sample-layers", type=int, default=1)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="write profiles/merge_bf16_traffic.txt from four rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE and WRITE_SIZE of this workload's bench run, then of --calibrate-copy "
+                         "--calibrate-mib MiB) and exit; needs no GPU")
+    ap.add_argument("--calibrate-mib", type=int, default=1024)
     return ap.parse_args()
 
 
@@ -54,13 +59,14 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, mode: str):
+def read_traffic(workload: str, mode: str, path=None):
     """HBM bytes per merge launch from the committed rocprofv3 counter summary, or
     None when the summary is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = path or TRAFFIC_FILE
+    if not os.path.exists(path):
         return None
     rec = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
@@ -70,6 +76,79 @@ def read_traffic(workload: str, mode: str):
         return float(rec["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def counter_mean(folder: str, counter: str, kernel_substr: str):
+    """Mean per dispatch of one rocprofv3 counter over the kernels whose name contains
+    kernel_substr, from the counter_collection.csv files under folder."""
+    import csv
+    import glob
+
+    total, dispatches, names = 0.0, set(), set()
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if kernel_substr in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                    total += float(row["Counter_Value"])
+                    dispatches.add(row.get("Dispatch_Id") or row.get("Correlation_Id"))
+                    names.add(row["Kernel_Name"])
+    if not dispatches:
+        raise SystemExit(f"no {counter} samples for '{kernel_substr}' under {folder}")
+    return total / len(dispatches), len(dispatches), sorted(names)
+
+
+def write_traffic(args, cfg, out=None):
+    """HBM bytes of one merge launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for torch.neg over a known size."""
+    out = out or TRAFFIC_FILE
+    fdir, wdir, cfdir, cwdir = args.traffic_from
+    f, nf, names = counter_mean(fdir, "FETCH_SIZE", "merge_bf16_kernel")
+    w, nw, _ = counter_mean(wdir, "WRITE_SIZE", "merge_bf16_kernel")
+    cf, ncf, _ = counter_mean(cfdir, "FETCH_SIZE", "neg")
+    cw, ncw, _ = counter_mean(cwdir, "WRITE_SIZE", "neg")
+    cal_kib = args.calibrate_mib * 1024.0
+    rf, wf = cal_kib / cf, cal_kib / cw
+    rd, wr = f * 1024 * rf, w * 1024 * wf
+    alg = cfg.merge_bytes()
+    mode = "out_of_place" if args.out_of_place else "in_place"
+    flags = (" --workload " + cfg.name if cfg.name != "llama7b_e8r16k2" else "") + \
+        (" --out-of-place" if args.out_of_place else "")
+    kname = names[0].replace("void ada::(anonymous namespace)::", "").split("(")[0]
+    lines = [
+        f"# HBM traffic of one merge launch (rocprofv3 counters), {cfg.name}, {mode.replace('_', ' ')}",
+        "#",
+        "# Commands (each a pass of its own, run from the repository root on one MI355X):",
+        "#   export TMPDIR=/tmp",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fdir} -o f -- python3 bench.py --steps 2 "
+        f"--warmup 1 --no-cpu-baseline --no-copy-ceiling{flags}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wdir} -o w -- python3 bench.py --steps 2 "
+        f"--warmup 1 --no-cpu-baseline --no-copy-ceiling{flags}",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfdir} -o f -- python3 bench.py "
+        f"--calibrate-copy {args.calibrate_mib}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwdir} -o w -- python3 bench.py "
+        f"--calibrate-copy {args.calibrate_mib}",
+        f"#   python3 bench.py{flags} --traffic-from {fdir} {wdir} {cfdir} {cwdir} --calibrate-mib {args.calibrate_mib}",
+        f"# Counter values are the mean per dispatch of the named kernel ({nf} / {nw} {kname} dispatches: merges "
+        f"and unmerges; {ncf} / {ncw} dispatches of torch's neg kernel for the calibration).",
+        "#",
+        f"# Calibration: torch.neg(a, out=b) on {args.calibrate_mib} MiB bf16 reads and writes exactly "
+        f"{cal_kib:.0f} KiB per launch.",
+        f"#   FETCH_SIZE read {cf:.1f} KiB -> read factor {rf:.4f}",
+        f"#   WRITE_SIZE read {cw:.1f} KiB -> write factor {wf:.4f}",
+        f"# Merge kernel: FETCH_SIZE {f:.1f} KiB, WRITE_SIZE {w:.1f} KiB per dispatch",
+        f"#   read  = {f:.1f} KiB x 1024 x {rf:.4f} = {rd:.0f} B",
+        f"#   write = {w:.1f} KiB x 1024 x {wf:.4f} = {wr:.0f} B",
+        f"#   total = {rd + wr:.0f} B per launch; algorithmic bytes {alg} B (ratio {(rd + wr) / alg:.4f})",
+        f"kernel_sha: {kernel_sha()}",
+        f"workload: {cfg.name}",
+        f"mode: {mode}",
+        f"read_bytes_per_launch: {rd:.0f}",
+        f"write_bytes_per_launch: {wr:.0f}",
+        f"traffic_bytes_per_launch: {rd + wr:.0f}",
+    ]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}: {rd + wr:.0f} B per launch ({(rd + wr) / alg:.4f} of algorithmic)")
 
 
 def pct(xs, q):
@@ -367,6 +446,10 @@ def run_e2e(args, cfg, torch, A, synth, dev):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        from weight_merge_amd.configs import PRESETS
+
+        return write_traffic(args, PRESETS[args.workload])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the merge needs no communication and this build runs on a "

@@ -1,0 +1,56 @@
+"""Host-side checks of bench.py: the one-GPU guard and the counter-summary round trip
+(synthetic rocprofv3 CSVs; no GPU)."""
+import argparse
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from weight_merge_amd.configs import PRESETS  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+
+
+def _csv(folder, rows):
+    os.makedirs(folder, exist_ok=True)
+    with open(os.path.join(folder, "x_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_traffic_summary_round_trip(tmp_path):
+    merge = "void ada::(anonymous namespace)::merge_bf16_kernel<32, 2, 4, 2, 0, false>(ada::MergeParams)"
+    neg = "void at::native::vectorized_elementwise_kernel<8, at::native::neg_kernel_cuda>(int)"
+    other = "void at::native::fill_kernel(int)"
+    d = {k: str(tmp_path / k) for k in ("f", "w", "cf", "cw")}
+    # two merge dispatches (1000 and 1200 KiB fetched, 2000 written) and an unrelated kernel
+    _csv(d["f"], [{"Dispatch_Id": 1, "Kernel_Name": merge, "Counter_Name": "FETCH_SIZE", "Counter_Value": 1000},
+                  {"Dispatch_Id": 2, "Kernel_Name": merge, "Counter_Name": "FETCH_SIZE", "Counter_Value": 1200},
+                  {"Dispatch_Id": 3, "Kernel_Name": other, "Counter_Name": "FETCH_SIZE", "Counter_Value": 9e9}])
+    _csv(d["w"], [{"Dispatch_Id": 1, "Kernel_Name": merge, "Counter_Name": "WRITE_SIZE", "Counter_Value": 2000}])
+    # calibration over 1 MiB: the fetch counter reads half, the write counter all of it
+    _csv(d["cf"], [{"Dispatch_Id": 5, "Kernel_Name": neg, "Counter_Name": "FETCH_SIZE", "Counter_Value": 512}])
+    _csv(d["cw"], [{"Dispatch_Id": 5, "Kernel_Name": neg, "Counter_Name": "WRITE_SIZE", "Counter_Value": 1024}])
+    args = argparse.Namespace(traffic_from=[d["f"], d["w"], d["cf"], d["cw"]], calibrate_mib=1, out_of_place=False)
+    cfg = PRESETS["llama7b_e8r16k2"]
+    out = str(tmp_path / "traffic.txt")
+    bench.write_traffic(args, cfg, out)
+    expect = 1100 * 1024 * 2.0 + 2000 * 1024 * 1.0
+    assert bench.read_traffic(cfg.name, "in_place", out) == pytest.approx(expect)
+    assert bench.read_traffic(cfg.name, "out_of_place", out) is None
+    assert bench.read_traffic("llama7b_e16r64k4", "in_place", out) is None
+    text = open(out).read().replace(bench.kernel_sha(), "0" * 16)
+    open(out, "w").write(text)
+    assert bench.read_traffic(cfg.name, "in_place", out) is None  # taken on another kernel source

@@ -10,7 +10,7 @@
 #include <new>
 #include <vector>
 
-#include "common.h"
+#include "launch.h"
 
 #ifndef ADA_LONG_TILE_GROUP
 #define ADA_LONG_TILE_GROUP 8

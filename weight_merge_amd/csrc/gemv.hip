@@ -11,7 +11,7 @@
 // route and apply adapters per layer, with several kernel calls per layer) keeps
 // the adapters separate: base GEMV (fp32 out), shrink t = A_sel x, expand
 // y = RNE(y32 + s * sum_j g_j B_j t_j).
-#include "common.h"
+#include "launch.h"
 
 namespace ada {
 namespace {

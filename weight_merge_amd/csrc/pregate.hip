@@ -11,7 +11,7 @@
 // score is summed in the same order whichever wave owns its row.  Wave 0 then holds
 // one score per lane (E <= 64) and runs k rounds of a wave-wide argmax on a 64-bit
 // key (order-preserving score bits, then the inverted lane index).
-#include "common.h"
+#include "launch.h"
 
 namespace ada {
 namespace {
