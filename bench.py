@@ -261,12 +261,24 @@ def simple_fusion_ms(torch, st, cfg, idx, gate, reps):
     return tot / reps
 
 
+def decode_groups(names):
+    """Projections of a layer that a decode step can run together: those reading the
+    same input.  In a decoder layer q, k and v read the normed hidden state, o reads the
+    attention output, gate and up the normed residual, down the activated MLP state."""
+    order = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    if sorted(names) == sorted(n for g in order for n in g):
+        return [[names.index(n) for n in g] for g in order]
+    return [[i] for i in range(len(names))]
+
+
 def run_e2e(args, cfg, torch, A, synth, dev):
     """End-to-end batch-1 request on the 7B-shaped stack: pregate + merge, decode steps
-    of one GEMV per projection through every layer, unmerge; against the unmerged
-    per-layer routed baseline (router + base GEMV + shrink + expand per projection,
-    every layer, every step) and the backbone alone.  Decode steps are timed eagerly
-    (Python-driven launches) and as one captured HIP graph per token."""
+    through every layer (one GEMV launch per group of projections that read the same
+    input), unmerge; against the unmerged per-layer routed baseline (router + base GEMV
+    + shrink + expand per projection, every layer, every step), the fused unmerged
+    comparator (router + two launches per group), the backbone alone, and a batch of
+    requests with mixed selections.  Decode steps are timed eagerly (Python-driven
+    launches) and as one captured HIP graph per token."""
     steps = cfg.decode_steps
     st = synth.make_stack(cfg, args.seed, device=dev)
     h, R = synth.router_inputs(cfg, args.seed)
@@ -283,7 +295,16 @@ def run_e2e(args, cfg, torch, A, synth, dev):
     ws = [[torch.empty((proj.d_out + cfg.kr + 3) // 4 * 4, dtype=torch.float32, device=dev)
            for proj in cfg.projections] for _ in range(cfg.n_layers)]
 
+    groups = decode_groups([proj.name for proj in cfg.projections])
+    names = [proj.name for proj in cfg.projections]
+
     def token_merged():
+        # one launch per group of projections that read the same input
+        for l in range(cfg.n_layers):
+            for grp in groups:
+                A.ada_decode_gemv_layer([(st.W[l][p], x[names[p]], ys[l][p]) for p in grp])
+
+    def token_merged_per_projection():
         for l, p, proj in st.items():
             A.ada_decode_gemv(st.W[l][p], x[proj.name], ys[l][p])
 
@@ -294,15 +315,16 @@ def run_e2e(args, cfg, torch, A, synth, dev):
                 A.ada_lora_apply(st.W[l][p], st.A[l][p], st.B[l][p], lidx[l], lgate[l], cfg.scale, x[proj.name],
                                  ys[l][p], ws[l][p])
 
-    lws = [torch.empty(A.lora_layer_workspace_elems([p.d_out for p in cfg.projections], cfg.k, cfg.r),
-                       dtype=torch.float32, device=dev) for _ in range(cfg.n_layers)]
+    lws = [[torch.empty(A.lora_layer_workspace_elems([cfg.projections[p].d_out for p in grp], cfg.k, cfg.r),
+                        dtype=torch.float32, device=dev) for grp in groups] for _ in range(cfg.n_layers)]
 
     def token_baseline_fused():
-        # the strongest unmerged comparator: router + two launches per layer
+        # the strongest unmerged comparator: router + two launches per group of a layer
         for l in range(cfg.n_layers):
             A.ada_pregate(h, R, cfg.k, cfg.renorm, lidx[l], lgate[l])
-            A.ada_lora_layer([(st.W[l][p], st.A[l][p], st.B[l][p], x[proj.name], ys[l][p])
-                              for p, proj in enumerate(cfg.projections)], lidx[l], lgate[l], cfg.scale, lws[l])
+            for gi, grp in enumerate(groups):
+                A.ada_lora_layer([(st.W[l][p], st.A[l][p], st.B[l][p], x[names[p]], ys[l][p]) for p in grp],
+                                 lidx[l], lgate[l], cfg.scale, lws[l][gi])
 
     def graph_of(fn):
         fn()
@@ -324,6 +346,9 @@ def run_e2e(args, cfg, torch, A, synth, dev):
     merged_eager = time_ms(torch, token_merged, reps)
     g_merged = graph_of(token_merged)
     merged_graph = time_ms(torch, g_merged.replay, reps)
+    g_merged_pp = graph_of(token_merged_per_projection)
+    merged_pp_graph = time_ms(torch, g_merged_pp.replay, reps)
+    del g_merged_pp
     A.ada_unmerge(model, idx, gate, cfg.scale)
     # N1: fused switch between two selections (undo prev + apply cur in one pass), and
     # N2: switching every decode token (each token pays a full switch)
@@ -368,13 +393,15 @@ def run_e2e(args, cfg, torch, A, synth, dev):
         xb = synth.decode_inputs(cfg, args.seed + 1, nb, device=dev)
         yb = [[torch.empty(nb, proj.d_out, dtype=torch.bfloat16, device=dev) for proj in cfg.projections]
               for _ in range(cfg.n_layers)]
-        bws = [torch.empty(A.lora_batch_workspace_elems([p.d_out for p in cfg.projections], nb, cfg.k, cfg.r),
-                           dtype=torch.float32, device=dev) for _ in range(cfg.n_layers)]
+        bws = [[torch.empty(A.lora_batch_workspace_elems([cfg.projections[p].d_out for p in grp], nb, cfg.k,
+                                                         cfg.r), dtype=torch.float32, device=dev)
+                for grp in groups] for _ in range(cfg.n_layers)]
 
         def token_batch():
             for l in range(cfg.n_layers):
-                A.ada_lora_batch([(st.W[l][p], st.A[l][p], st.B[l][p], xb[proj.name], yb[l][p])
-                                  for p, proj in enumerate(cfg.projections)], bidx, bgate, cfg.scale, bws[l])
+                for gi, grp in enumerate(groups):
+                    A.ada_lora_batch([(st.W[l][p], st.A[l][p], st.B[l][p], xb[names[p]], yb[l][p]) for p in grp],
+                                     bidx, bgate, cfg.scale, bws[l][gi])
 
         g_batch = graph_of(token_batch)
         t_batch = time_ms(torch, g_batch.replay, reps)
@@ -391,7 +418,7 @@ def run_e2e(args, cfg, torch, A, synth, dev):
         }
         del yb, bws, xb
 
-    launches_merged = cfg.n_layers * len(cfg.projections)
+    launches_merged = cfg.n_layers * len(groups)
     launches_base = cfg.n_layers * (1 + 3 * len(cfg.projections))
     req_graph = t_pregate + pair + steps * merged_graph
     req_base_graph = steps * base_graph
@@ -415,6 +442,7 @@ def run_e2e(args, cfg, torch, A, synth, dev):
             "merge_plus_unmerge": round(pair, 3),
             "token_backbone_graph": round(backbone_graph, 4),
             "token_merged_graph": round(merged_graph, 4),
+            "token_merged_per_projection_graph": round(merged_pp_graph, 4),
             "token_baseline_graph": round(base_graph, 4),
             "token_backbone_eager": round(backbone_eager, 4),
             "token_merged_eager": round(merged_eager, 4),
@@ -432,8 +460,10 @@ def run_e2e(args, cfg, torch, A, synth, dev):
             "request_switch_every_token_eager": round(steps * per_token_switch + t_pregate, 3),
         },
         "decode_GBps_merged_graph": round(token_bytes / (merged_graph * 1e-3) / 1e9, 1),
-        "launches_per_token": {"merged": launches_merged, "baseline": launches_base,
-                               "fused_unmerged": cfg.n_layers * 3},
+        "launches_per_token": {"merged": launches_merged, "merged_per_projection": cfg.n_layers * len(names),
+                               "baseline": launches_base, "fused_unmerged": cfg.n_layers * (1 + 2 * len(groups)),
+                               "batch_mixed_selections": cfg.n_layers * 2 * len(groups)},
+        "decode_groups": [[names[p] for p in grp] for grp in groups],
         "speedup_request_vs_fused_unmerged_graph": round(steps * fused_graph / req_graph, 3),
         "break_even_tokens_graph": None if be is None else round(be, 1),
         "speedup_request_graph": round(req_base_graph / req_graph, 3),

@@ -18,7 +18,8 @@
  *   - Every tensor pointer is a DEVICE pointer unless stated otherwise, 16-byte
  *     aligned, row-major, owned by the caller.  The library never allocates or
  *     frees caller memory, and the hot calls (pregate, merge, unmerge, switch,
- *     decode_gemv, lora_apply, lora_layer, lora_batch) allocate nothing at all.
+ *     decode_gemv, decode_gemv_layer, lora_apply, lora_layer, lora_batch) allocate
+ *     nothing at all.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *     calls are asynchronous on that stream and return once the work is enqueued.
  *   - Return value: ADA_OK (0) or a negative ada_status.  All argument checks run
@@ -142,6 +143,25 @@ int ada_switch(ada_model m, const int32_t* idx_prev, const float* gate_prev, int
  */
 int ada_decode_gemv(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w,
                     const void* x, void* y, int32_t dtype, void* stream);
+
+/* One decode GEMV for ada_decode_gemv_layer. */
+typedef struct {
+  const void* w;    /* [d_out][ld_w] weights                         */
+  const void* x;    /* [d_in] input                                   */
+  void* y;          /* [d_out] output                                 */
+  int32_t d_out;
+  int32_t d_in;
+  int64_t ld_w;
+} ada_gemv_proj;
+
+/*
+ * Up to 16 independent decode GEMVs (for instance the q, k and v projections of a
+ * layer, which read the same hidden state) in ONE launch: y_p = RNE(w_p @ x_p) for
+ * every p, each bit-identical to ada_decode_gemv on the same operands.  Fewer launches
+ * per decode step leave less launch ramp and tail, which the small projections of a
+ * batch-1 step are bound by.
+ */
+int ada_decode_gemv_layer(const ada_gemv_proj* projs, int32_t n_proj, int32_t dtype, void* stream);
 
 /*
  * One projection of the conventional, unmerged dynamic-adapter layer the pages

@@ -203,3 +203,22 @@ def test_lora_batch_validation(lib):
     assert f(arr(x=MIS), 1, nb, 4, 8, P, P2, 2, 2.0, P, ws, ADA_BF16, None) == ADA_EALIGN
     assert f(arr(), 1, nb, 4, 8, P, P2, 2, 2.0, P, ws - 16, ADA_BF16, None) == ADA_ESHAPE
     assert f(arr(), 1, nb, 4, 8, P, P2, 2, 2.0, MIS, ws, ADA_BF16, None) == ADA_EALIGN
+
+
+def test_decode_gemv_layer_validation(lib):
+    from weight_merge_amd._lib import AdaGemvProj
+
+    def arr(n=1, **kw):
+        a = dict(dict(w=P, x=P2, y=P, d_out=64, d_in=64, ld_w=64), **kw)
+        return (AdaGemvProj * n)(*[AdaGemvProj(a["w"], a["x"], a["y"], a["d_out"], a["d_in"], a["ld_w"])] * n)
+
+    f = lib.ada_decode_gemv_layer
+    assert f(None, 1, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(), 1, 9, None) == ADA_EDTYPE
+    assert f(arr(), 0, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(17), 17, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(w=None), 1, ADA_BF16, None) == ADA_EINVAL
+    assert f(arr(y=MIS), 1, ADA_BF16, None) == ADA_EALIGN
+    assert f(arr(d_in=60), 1, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(ld_w=32), 1, ADA_BF16, None) == ADA_ESHAPE
+    assert f(arr(ld_w=68), 1, ADA_BF16, None) == ADA_EALIGN

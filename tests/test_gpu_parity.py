@@ -487,3 +487,23 @@ def test_lora_batch_serves_a_selection_per_request(dt, E, r, k, nb):
                                         np.array([g for _, g in keep], dtype=np.float64), 2.0, to64(x[bq]))
             err = np.abs(to64(got) - ref)
             assert np.all(err <= gemv_bound(W64, x64, ref, dt) + 1e-4 * (np.abs(W64) @ np.abs(x64))), (bq, pi)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_decode_gemv_layer_is_the_per_projection_gemv(dt):
+    """Independent GEMVs in one launch: each bit-identical to its own ada_decode_gemv
+    and within the GEMV bound of the oracle."""
+    shapes = [(264, 520), (1032, 264), (8, 8), (136, 1000), (520, 136)]
+    mats = [synth.adapter_bank(600 + i, 1, 8, do, di, dt)[0] for i, (do, di) in enumerate(shapes)]
+    xs = [synth.host_normal(synth.tensor_seed(700 + i, di), (di,), 1.0, dt) for i, (_, di) in enumerate(shapes)]
+    dev = [(W.to(DEV), x.to(DEV)) for W, x in zip(mats, xs)]
+    ys = [torch.full((W.shape[0],), float("nan"), dtype=TD[dt], device=DEV) for W in mats]
+    A.ada_decode_gemv_layer([(w, x, y) for (w, x), y in zip(dev, ys)])
+    one = [A.ada_decode_gemv(w, x) for w, x in dev]
+    sync()
+    iv = torch.int16 if dt == "bf16" else torch.int32
+    for W, x, y, y1 in zip(mats, xs, ys, one):
+        assert torch.equal(y.cpu().view(iv), y1.cpu().view(iv))
+        W64, x64 = to64(W), to64(x)
+        ref = O.gemv(W64, x64)
+        assert np.all(np.abs(to64(y) - ref) <= gemv_bound(W64, x64, ref, dt))

@@ -8,6 +8,7 @@ from .api import (  # noqa: F401
     AdaError,
     AdaModel,
     ada_decode_gemv,
+    ada_decode_gemv_layer,
     ada_lora_apply,
     ada_lora_batch,
     ada_lora_layer,

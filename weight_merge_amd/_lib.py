@@ -40,6 +40,17 @@ class AdaLoraProj(ctypes.Structure):
     ]
 
 
+class AdaGemvProj(ctypes.Structure):
+    _fields_ = [
+        ("w", c_void_p),
+        ("x", c_void_p),
+        ("y", c_void_p),
+        ("d_out", c_int32),
+        ("d_in", c_int32),
+        ("ld_w", c_int64),
+    ]
+
+
 _SIGNATURES = {
     "ada_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ada_model_create": (ctypes.c_int, [ctypes.POINTER(AdaProj), c_int32, c_int32, c_int32, c_int32,
@@ -54,6 +65,7 @@ _SIGNATURES = {
                                   c_float, c_void_p]),
     "ada_decode_gemv": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_void_p, c_int32,
                                        c_void_p]),
+    "ada_decode_gemv_layer": (ctypes.c_int, [ctypes.POINTER(AdaGemvProj), c_int32, c_int32, c_void_p]),
     "ada_lora_apply": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_void_p, c_int32,
                                       c_int32, c_void_p, c_void_p, c_int32, c_float, c_void_p, c_void_p,
                                       c_void_p, c_int64, c_int32, c_void_p]),

@@ -12,7 +12,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import ADA_BF16, ADA_F32, AdaLoraProj, AdaProj
+from ._lib import ADA_BF16, ADA_F32, AdaGemvProj, AdaLoraProj, AdaProj
 
 _DT = {torch.float32: ADA_F32, torch.bfloat16: ADA_BF16}
 
@@ -178,6 +178,27 @@ def ada_decode_gemv(w: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = N
                                      _dtype(w), _stream(stream))
     _check(st, "ada_decode_gemv")
     return y
+
+
+def ada_decode_gemv_layer(projs, stream=None):
+    """Independent GEMVs y_p = W_p x_p in one launch; projs: list of (w, x, y) with w
+    [d_out, d_in], x [d_in], y [d_out] (written), all of one dtype."""
+    projs = list(projs)
+    arr = (AdaGemvProj * len(projs))()
+    dt = projs[0][0].dtype
+    for i, (w, x, y) in enumerate(projs):
+        d_out, d_in = w.shape
+        if w.stride(1) != 1:
+            raise ValueError("w must have unit column stride")
+        _contig(x, "x")
+        _contig(y, "y")
+        if x.shape != (d_in,) or y.shape != (d_out,):
+            raise ValueError("x must be [d_in] and y [d_out]")
+        if w.dtype != dt or x.dtype != dt or y.dtype != dt:
+            raise TypeError("all tensors share one dtype")
+        arr[i] = AdaGemvProj(_dev(w, "w"), _dev(x, "x"), _dev(y, "y"), d_out, d_in, w.stride(0))
+    st = _lib.load().ada_decode_gemv_layer(arr, len(projs), _DT[dt], _stream(stream))
+    _check(st, "ada_decode_gemv_layer")
 
 
 def ada_lora_apply(w, a, b, idx, gate, scale: float, x, y=None, workspace=None, stream=None):

@@ -291,6 +291,35 @@ int ada_decode_gemv(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w, co
   return e == hipSuccess ? ADA_OK : ADA_EHIP;
 }
 
+int ada_decode_gemv_layer(const ada_gemv_proj* projs, int32_t n_proj, int32_t dtype, void* stream) {
+  if (projs == nullptr) return ADA_EINVAL;
+  if (!dtype_ok(dtype)) return ADA_EDTYPE;
+  if (n_proj < 1 || n_proj > ada::kMaxLayerProj) return ADA_ESHAPE;
+  const int esz = dtype == ADA_BF16 ? 2 : 4;
+  ada::GemvLayerParams p{};
+  int64_t rows = 0;
+  for (int32_t i = 0; i < n_proj; ++i) {
+    const ada_gemv_proj& q = projs[i];
+    if (q.w == nullptr || q.x == nullptr || q.y == nullptr) return ADA_EINVAL;
+    if (!aligned16(q.w) || !aligned16(q.x) || !aligned16(q.y)) return ADA_EALIGN;
+    if (!dim_ok(q.d_out) || !dim_ok(q.d_in) || q.ld_w < q.d_in || q.ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
+    if ((q.ld_w * esz) % 16 != 0) return ADA_EALIGN;
+    ada::GemvLayerProj& P = p.proj[i];
+    P.w = q.w;
+    P.x = q.x;
+    P.y = q.y;
+    P.ld = q.ld_w;
+    P.d_out = q.d_out;
+    P.d_in = q.d_in;
+    P.row0 = static_cast<int32_t>(rows);
+    rows += q.d_out;
+  }
+  if (rows >= (int64_t(1) << 30)) return ADA_ESHAPE;
+  p.n = n_proj;
+  const hipError_t e = ada::launch_gemv_layer(p, static_cast<int>(rows), dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : ADA_EHIP;
+}
+
 int ada_lora_apply(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w, const void* a,
                    const void* b, int32_t E, int32_t r, const int32_t* idx, const float* gate,
                    int32_t k, float scale, const void* x, void* y, void* workspace,

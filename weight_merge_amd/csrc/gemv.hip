@@ -102,6 +102,23 @@ __global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ W, int 
   }
 }
 
+// Independent GEMVs in one grid (the stacked rows of every projection, one row per
+// wave): per projection bit-identical to gemv_kernel, with one launch's ramp and tail
+// instead of one per projection.
+template <typename T>
+__global__ void __launch_bounds__(256) gemv_layer_kernel(GemvLayerParams p) {
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int q = 0;
+  while (q < p.n - 1 && g >= p.proj[q + 1].row0) ++q;
+  const GemvLayerProj& P = p.proj[q];
+  const int row = g - P.row0;
+  if (row >= P.d_out) return;
+  const float s = row_dot<T, kGemvBatch>(static_cast<const T*>(P.w) + int64_t(row) * P.ld,
+                                         static_cast<const T*>(P.x), P.d_in);
+  if (lane == 0) store_out(static_cast<T*>(P.y), row, s);
+}
+
 // t[j*r + rr] = A[idx_j][rr] . x for every slot j < k (0 for an out-of-range index).
 template <typename T>
 __global__ void __launch_bounds__(256) lora_shrink_kernel(const T* __restrict__ A, int E, int r,
@@ -311,6 +328,15 @@ hipError_t launch_gemv(const void* w, int d_out, int d_in, int64_t ld, const voi
   else
     hipLaunchKernelGGL((gemv_kernel<float>), grid, block, 0, s, static_cast<const float*>(w), d_out, d_in,
                        ld, static_cast<const float*>(x), static_cast<float*>(y), y32);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_layer(const GemvLayerParams& p, int rows, int dtype, hipStream_t s) {
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(gemv_layer_kernel<uint16_t>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(gemv_layer_kernel<float>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -6,11 +6,30 @@
 
 namespace ada {
 
+constexpr int kMaxLayerProj = 16;  // projections of one layer launch
+
 hipError_t launch_pregate(const void* h, const void* router, int d, int E, int k, int dtype,
                           int renorm, int32_t* idx, float* gate, hipStream_t s);
 
 hipError_t launch_gemv(const void* w, int d_out, int d_in, int64_t ld, const void* x, void* y,
                        float* y32, int dtype, hipStream_t s);
+
+// Several independent decode GEMVs (at most kMaxLayerProj, passed by value) in one grid:
+// row0 is the projection's first row in the stacked rows.
+struct GemvLayerProj {
+  const void* w;
+  const void* x;
+  void* y;
+  int64_t ld;
+  int32_t d_out;
+  int32_t d_in;
+  int32_t row0;
+};
+struct GemvLayerParams {
+  GemvLayerProj proj[kMaxLayerProj];
+  int32_t n;
+};
+hipError_t launch_gemv_layer(const GemvLayerParams& p, int rows, int dtype, hipStream_t s);
 
 hipError_t launch_lora_shrink(const void* a, int E, int r, int d_in, const int32_t* idx, int k,
                               const void* x, float* t, int dtype, hipStream_t s);
@@ -21,7 +40,6 @@ hipError_t launch_lora_expand(const void* b, int E, int r, int d_out, const int3
 
 // One layer of the unmerged routed path (at most kMaxLayerProj projections, passed
 // by value so the launch needs no device table).
-constexpr int kMaxLayerProj = 16;
 struct LoraLayerProj {
   const void* w;
   const void* a;
