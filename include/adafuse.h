@@ -209,7 +209,7 @@ int ada_lora_layer(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_
  * so requests with different selections are served unmerged:
  *   y_b = RNE(w @ x_b + scale * sum_j gate[b][j] * B[idx[b][j]] (A[idx[b][j]] x_b)).
  * Every W row is read once for the whole batch (the base product runs on MFMA, 16
- * rows by 16 requests per wave).  Per projection, x is [nb][d_in] and y is
+ * rows by 16 requests per workgroup).  Per projection, x is [nb][d_in] and y is
  * [nb][d_out] (rows contiguous); idx and gate are device arrays [nb][k].  Request
  * b's result equals ada_lora_layer on (x_b, idx[b], gate[b]) up to the order of the
  * base product's fp32 sums.  `workspace`: caller-owned device memory of at least

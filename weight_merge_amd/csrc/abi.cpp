@@ -426,7 +426,7 @@ int ada_lora_batch(const ada_lora_proj* projs, int32_t n_proj, int32_t nb, int32
     P.dot_row0 = static_cast<int32_t>(dot_rows);
     P.out_row0 = static_cast<int32_t>(out_rows);
     P.ws_off = ws;
-    dot_rows += (q.d_out + 15) / 16 + nb * kr;  // waves: 16 W rows per base wave, one shrink row per wave
+    dot_rows += (q.d_out + 15) / 16 + (nb * kr + 3) / 4;  // workgroups: 16 W rows each, then 4 shrink rows each
     out_rows += int64_t(nb) * q.d_out;
     ws = (ws + nb * (q.d_out + kr) + 3) & ~int64_t(3);  // keep every block 16-byte aligned
   }

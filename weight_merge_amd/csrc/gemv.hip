@@ -207,29 +207,32 @@ __global__ void __launch_bounds__(256) lora_layer_expand_kernel(LoraLayerParams 
                        ws + P.d_out));
 }
 
-// ---- a batch of requests, each with its own selection (one layer, two launches).
-// Grid 1, in units of waves: per projection, ceil(d_out/16) waves for the base product
-// and nb*k*r waves for the shrink rows.  A base wave computes Y[16 rows][16 requests]
-// = W[rows] X^T on MFMA (v_mfma_f32_16x16x32_bf16; fp32: 16x16x4), so each W row is
-// read from HBM once for the whole batch and each request's activations once per 16
-// rows.  Lane l = 16 q + i supplies W[row i][k .. k+7] and X[request i][k .. k+7]
-// (k = k0 + 8 q) and receives D[4 q + c][i] = sum_k W[row 4q + c][k] X[request i][k].
-// Rows past d_out and requests past nb re-read row / request 0 and are not stored.
+// ---- a batch of requests, each with its own selection (one group of a layer's
+// projections, two launches).  Grid 1, in units of workgroups: per projection,
+// ceil(d_out/16) base workgroups, then ceil(nb*k*r / 4) shrink workgroups (one selected
+// A row per wave).  A base workgroup computes Y[16 rows][16 requests] = W[rows] X^T on
+// MFMA (v_mfma_f32_16x16x32_bf16; fp32: 16x16x4), its 4 waves taking interleaved
+// slices of the contraction and adding their partial tiles in a fixed order through
+// LDS, so each W row is read from HBM once for the whole batch.  Lane l = 16 q + i of
+// a wave supplies W[row i][k .. k+7] and X[request i][k .. k+7] (k = k0 + 8 q) and
+// receives D[4 q + c][i] = sum_k W[row 4q + c][k] X[request i][k].  Rows past d_out
+// and requests past nb re-read row / request 0 and are not stored.
 // Grid 2: every request's expand (as ada_lora_layer).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// One wave's share of a base tile: contraction steps wave, wave + 4, wave + 8, ...
 template <typename T>
-__device__ __forceinline__ f32x4 base_tile(const T* __restrict__ W, int64_t ld, int row0, int d_out,
-                                           const T* __restrict__ X, int d_in, int nb) {
+__device__ __forceinline__ f32x4 base_tile_part(const T* __restrict__ W, int64_t ld, int row0, int d_out,
+                                                const T* __restrict__ X, int d_in, int nb, int wave) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, i = lane & 15;
   const T* wrow = W + int64_t(row0 + i < d_out ? row0 + i : 0) * ld;
   const T* xrow = X + int64_t(i < nb ? i : 0) * d_in;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (sizeof(T) == 2) {
-    constexpr int U = 4;  // 32-deep steps in flight
-    for (int k0 = 0; k0 < d_in; k0 += 32 * U) {
+    constexpr int U = 4;  // 32-deep steps in flight per wave
+    for (int k0 = 32 * U * wave; k0 < d_in; k0 += 4 * 32 * U) {
       uint4 wv[U], xv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -249,7 +252,7 @@ __device__ __forceinline__ f32x4 base_tile(const T* __restrict__ W, int64_t ld, 
   } else {
     // fp32: lane (q, i) loads 4 consecutive k; MFMA j takes element j of every lane,
     // i.e. k = k0 + 4 q + j (the same permutation of k on both operands)
-    for (int k0 = 0; k0 < d_in; k0 += 16) {
+    for (int k0 = 16 * wave; k0 < d_in; k0 += 4 * 16) {
       const int k = k0 + 4 * q;
       const bool in = k < d_in;  // d_in is a multiple of 8: whole 4-vectors in or out
       const float4 w = *reinterpret_cast<const float4*>(wrow + (in ? k : 0));
@@ -267,20 +270,27 @@ __device__ __forceinline__ f32x4 base_tile(const T* __restrict__ W, int64_t ld, 
 
 template <typename T>
 __global__ void __launch_bounds__(256) lora_batch_dot_kernel(LoraLayerParams p) {
+  __shared__ f32x4 part[3][64];
   const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave index
+  const int wave = threadIdx.x >> 6;
+  const int g = blockIdx.x;  // workgroup index
   int q = 0;
   while (q < p.n - 1 && g >= p.proj[q + 1].dot_row0) ++q;
   const LoraLayerProj& P = p.proj[q];
   const int lw = g - P.dot_row0;
   const int kr = p.k * p.r;
-  const int base_waves = (P.d_out + 15) / 16;
-  if (lw >= base_waves + p.nb * kr) return;
+  const int base_wgs = (P.d_out + 15) / 16;
   const T* x = static_cast<const T*>(P.x);
   float* ws = p.ws + P.ws_off;
-  if (lw < base_waves) {
+  if (lw < base_wgs) {
     const int row0 = 16 * lw;
-    const f32x4 acc = base_tile(static_cast<const T*>(P.w), P.ld, row0, P.d_out, x, P.d_in, p.nb);
+    f32x4 acc = base_tile_part(static_cast<const T*>(P.w), P.ld, row0, P.d_out, x, P.d_in, p.nb, wave);
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    acc = acc + part[0][lane];
+    acc = acc + part[1][lane];
+    acc = acc + part[2][lane];
     const int i = lane & 15, qq = lane >> 4;
     if (i < p.nb) {
 #pragma unroll
@@ -290,7 +300,8 @@ __global__ void __launch_bounds__(256) lora_batch_dot_kernel(LoraLayerParams p) 
       }
     }
   } else {
-    const int sr = lw - base_waves;  // request b, slot j, rank rr
+    const int sr = 4 * (lw - base_wgs) + wave;  // request b, slot j, rank rr
+    if (sr >= p.nb * kr) return;
     const int b = sr / kr, rem = sr - b * kr, j = rem / p.r, rr = rem - j * p.r;
     const int e = p.idx[b * p.k + j];
     float s = 0.f;
@@ -377,8 +388,8 @@ hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_row
   return hipGetLastError();
 }
 
-hipError_t launch_lora_batch(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s) {
-  const dim3 g1((dot_rows + 3) / 4), g2((out_rows + 255) / 256), block(256);
+hipError_t launch_lora_batch(const LoraLayerParams& p, int dot_wgs, int out_rows, int dtype, hipStream_t s) {
+  const dim3 g1(dot_wgs), g2((out_rows + 255) / 256), block(256);
   if (dtype == 1) {
     hipLaunchKernelGGL(lora_batch_dot_kernel<uint16_t>, g1, block, 0, s, p);
     hipLaunchKernelGGL(lora_batch_expand_kernel<uint16_t>, g2, block, 0, s, p);

@@ -67,12 +67,12 @@ struct LoraLayerParams {
 };
 hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s);
 
-// A batch of requests with a selection each, one layer (the unmerged path serving mixed
-// selections).  Per projection x is [nb][d_in], y [nb][d_out]; dot_row0 counts waves of
-// the first grid: ceil(d_out / 16) base waves (16 W rows for every request) then
-// nb * k*r shrink rows; out_row0 indexes the nb * d_out outputs; ws_off is an fp32
-// block of nb * (d_out + k*r).
+// A batch of requests with a selection each, one group of projections (the unmerged
+// path serving mixed selections).  Per projection x is [nb][d_in], y [nb][d_out];
+// dot_row0 counts workgroups of the first grid: ceil(d_out / 16) base workgroups (16 W
+// rows for every request) then ceil(nb * k*r / 4) shrink workgroups; out_row0 indexes
+// the nb * d_out outputs; ws_off is an fp32 block of nb * (d_out + k*r).
 constexpr int kMaxBatch = 16;
-hipError_t launch_lora_batch(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s);
+hipError_t launch_lora_batch(const LoraLayerParams& p, int dot_wgs, int out_rows, int dtype, hipStream_t s);
 
 }  // namespace ada
