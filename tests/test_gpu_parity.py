@@ -272,12 +272,13 @@ def test_merge_then_unmerge_returns_w(inplace):
         assert torch.equal(w.cpu(), W)
 
 
-@pytest.mark.parametrize("r", [16, 32])
-def test_switch_matches_oracle(r):
-    E = 8
+@pytest.mark.parametrize("r,E,kp,kc", [(16, 8, 2, 3), (32, 8, 2, 3), (128, 4, 2, 2), (8, 64, 32, 32)])
+def test_switch_matches_oracle(r, E, kp, kc):
+    """Undo one selection and apply another in one pass, up to the largest contraction
+    one launch takes ((k_prev + k_cur) * r = 512, in 4 or in 64 slots)."""
     W, Aw, Bw = synth.adapter_bank(43, E, r, 264, 520, "bf16")
-    pi, pg = make_selection(E, 2, 64, "bf16", 7)
-    ci, cg = make_selection(E, 3, 64, "bf16", 8)
+    pi, pg = make_selection(E, kp, 64, "bf16", 7)
+    ci, cg = make_selection(E, kc, 64, "bf16", 8)
     ref = O.switch(to64(W), to64(Aw), to64(Bw), (pi.numpy(), pg.numpy().astype(np.float64)),
                    (ci.numpy(), cg.numpy().astype(np.float64)), 2.0)
     w = W.to(DEV)
