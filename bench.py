@@ -51,11 +51,23 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments or blank lines (the merge sources hold no string
+    literal containing a comment marker)."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_sha() -> str:
+    """Identity of the merge kernel's code (merge.hip and common.h, comments aside):
+    a counter summary taken on another code is not reported."""
     h = hashlib.sha256()
     for f in ("merge.hip", "common.h"):
-        with open(os.path.join(ROOT, "weight_merge_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "weight_merge_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

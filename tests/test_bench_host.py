@@ -54,3 +54,9 @@ def test_traffic_summary_round_trip(tmp_path):
     text = open(out).read().replace(bench.kernel_sha(), "0" * 16)
     open(out, "w").write(text)
     assert bench.read_traffic(cfg.name, "in_place", out) is None  # taken on another kernel source
+
+
+def test_kernel_identity_ignores_comments():
+    code = "int f(int x) {\n  return x + 1;  // add one\n}\n"
+    assert bench._code_only(code) == bench._code_only("/* doc\n   more */\n" + code.replace("// add one", "// +1"))
+    assert bench._code_only(code) != bench._code_only(code.replace("+ 1", "+ 2"))

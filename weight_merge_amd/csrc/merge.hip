@@ -24,9 +24,11 @@
 //     buffered), with the gate and scale folded into B_cat (rounded to bf16).  Both
 //     are stored as they lie in memory (16-byte writes); the A operand's transpose
 //     happens in the LDS read (ds_read_b64_tr_b16).
-//   * The W loads are issued first, straight after the tile lookup, with every load
-//     on the path branch-free and in the global address space, so no wait for the
-//     selection or the adapter gathers also waits for the W tile.
+//   * The W loads are issued straight after the tile lookup and the selection loads,
+//     with every load on the path branch-free and in the global address space, so
+//     compacting the selection does not wait for the W tile (the vector-memory
+//     counter is in order: the adapter gathers, issued after W, do wait for it, and
+//     the K loop starts once both have arrived).
 //   * Small tiles (64 x 128) keep registers low for short contractions: four waves
 //     per SIMD, so many tiles' W loads are in flight on each CU.  Long contractions
 //     (k*r > 64) use 128 x 128 tiles so each gathered adapter byte serves more weights.
