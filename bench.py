@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_e8r16k2",
-                    help="preset: llama7b_e8r16k2 (default), llama7b_e16r64k4, llama70b_e8r16k2, tiny")
+                    help="preset: llama7b_e8r16k2 (default), llama7b_e16r64k4, llama70b_e8r16k2, "
+                         "llama70b_tp8_e8r16k2, e2e_llama7b, tiny")
     ap.add_argument("--out-of-place", action="store_true", help="merge into a separate W' buffer")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")

@@ -11,7 +11,7 @@ from helpers import (BF16_ATOL, BF16_RTOL, GATE_ATOL, GATE_RTOL, check_close, ga
 from oracle import adafuse as O
 from weight_merge_amd import api as A
 from weight_merge_amd import synth
-from weight_merge_amd.configs import LLAMA7B_E8R16K2, LLAMA7B_E16R64K4, LLAMA70B_E8R16K2
+from weight_merge_amd.configs import LLAMA7B_E8R16K2, LLAMA7B_E16R64K4, LLAMA70B_E8R16K2, LLAMA70B_TP8_E8R16K2
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -71,4 +71,11 @@ def test_llama7b_e16r64k4_stack():
 def test_llama70b_e8r16k2_stack():
     # element by element: the k and v projections (1024 x 8192) of layer 0
     frac = run_stack(LLAMA70B_E8R16K2, 3000, lambda l, p, proj: l == 0 and proj.name in ("k", "v"))
+    assert frac > 0.8
+
+
+def test_llama70b_tp8_shard_stack():
+    # one GPU's tensor-parallel shard: element by element, the 128-row k and v projections
+    # and the 1024-column o projection of layer 0
+    frac = run_stack(LLAMA70B_TP8_E8R16K2, 4000, lambda l, p, proj: l == 0 and proj.name in ("k", "v", "o"))
     assert frac > 0.8

@@ -121,6 +121,30 @@ LLAMA70B_E8R16K2 = StackConfig(
          "down 8192x28672), bf16, E=8, rank 16, top-2, merged in place then unmerged",
 )
 
+# One GPU's share of the 70B stack under 8-way tensor parallelism: the column-parallel
+# projections (q, k, v, gate, up) keep 1/8 of the output rows of W and of every B with
+# the full A; the row-parallel ones (o, down) keep 1/8 of the input columns of W and of
+# every A with the full B.  The merge needs no exchange, so this is the whole of one
+# GPU's merge.
+_L70_TP8 = (
+    Projection("q", 8192 // 8, 8192),
+    Projection("k", 1024 // 8, 8192),
+    Projection("v", 1024 // 8, 8192),
+    Projection("o", 8192, 8192 // 8),
+    Projection("gate", 28672 // 8, 8192),
+    Projection("up", 28672 // 8, 8192),
+    Projection("down", 8192, 28672 // 8),
+)
+
+LLAMA70B_TP8_E8R16K2 = StackConfig(
+    name="llama70b_tp8_e8r16k2",
+    n_layers=80, projections=_L70_TP8, d_model=8192,
+    E=8, r=16, k=2, scale=2.0, dtype="bf16", inplace=True,
+    note="one GPU's shard of the Llama-2-70B-shaped stack under 8-way tensor parallelism "
+         "(80 x q 1024x8192, k,v 128x8192, o 8192x1024, gate,up 3584x8192, down 8192x3584), "
+         "bf16, E=8, rank 16, top-2, in place",
+)
+
 E2E_7B = StackConfig(
     name="e2e_llama7b",
     n_layers=32, projections=_L7, d_model=4096,
@@ -130,7 +154,8 @@ E2E_7B = StackConfig(
          "GEMVs through every projection, unmerge; vs a per-layer routed unmerged baseline",
 )
 
-PRESETS = {c.name: c for c in (TINY, LLAMA7B_E8R16K2, LLAMA7B_E16R64K4, LLAMA70B_E8R16K2, E2E_7B)}
+PRESETS = {c.name: c for c in (TINY, LLAMA7B_E8R16K2, LLAMA7B_E16R64K4, LLAMA70B_E8R16K2,
+                                LLAMA70B_TP8_E8R16K2, E2E_7B)}
 
 
 def scaled(cfg: StackConfig, n_layers: int) -> StackConfig:
