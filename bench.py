@@ -25,6 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+VALU_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector peak
 METRIC = "full-model adapter merge: effective HBM GB/s (% of peak) and merge µs"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "merge_bf16_traffic.txt")
 
@@ -625,6 +627,17 @@ def main():
             "traffic": None if traffic is None else int(traffic),
             "kernel": "merge_bf16_kernel" if cfg.dtype == "bf16" else "merge_f32_kernel",
             "kernel_sha": kernel_sha(),
+        },
+        # the rank-k*r product (secondary: the merge is bound by HBM): bf16 runs it on
+        # MFMA (dense bf16 peak), fp32 storage on the vector ALUs (fp32 vector peak)
+        "contraction": {
+            "engine": "mfma" if cfg.dtype == "bf16" else "valu",
+            "flops": cfg.merge_flops(),
+            "achieved": round(cfg.merge_flops() / merge_mean_s / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else VALU_F32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(cfg.merge_flops() / merge_mean_s / 1e12
+                          / (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else VALU_F32_PEAK_TFLOPS), 4),
         },
         "cpu_baseline": cpu,
     }
