@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from helpers import (BF16_ATOL, BF16_RTOL, GATE_ATOL, GATE_RTOL, check_close, folded_bound, gapped_router,
-                     min_gap, oracle_selection, to64, tol)
+                     min_gap, oracle_selection, sample_rows, to64, tol)
 from oracle import adafuse as O
 from weight_merge_amd import api as A
 from weight_merge_amd import synth
@@ -118,6 +118,44 @@ def test_merge_matches_oracle(E, r, k, d_out, d_in, dt, inplace):
     check_close(got, ref, *tol(TD[dt]), "merge")
     if not inplace:
         assert torch.equal(w.cpu(), W), "out-of-place merge must not write W"
+
+
+# W and each adapter bank are addressed with 32-bit byte offsets; the library admits
+# operands of fewer than 2^31 elements.  One operand per case sits just under that.
+LIMIT_CASES = [
+    # E, r, k, d_out, d_in, operand at the limit
+    (2, 16, 2, 32768, 65528, "W"),   # W: 2,147,221,504 elements (64 x 128 tiles)
+    (64, 256, 1, 8, 131064, "A"),    # A: 64 x 256 x 131064 = 2,147,352,576 elements (128 x 128 tiles)
+    (64, 256, 1, 131064, 8, "B"),    # B: the same count
+]
+
+
+@pytest.mark.parametrize("E,r,k,d_out,d_in,big", LIMIT_CASES)
+def test_operands_at_the_32_bit_offset_limit(E, r, k, d_out, d_in, big):
+    """The last expert is selected, so the gathers reach the top of the banks; the
+    checked rows include the last rows of W."""
+    assert max(d_out * d_in, E * r * d_in, E * r * d_out) < 2 ** 31
+    seed = 11
+    w = synth.device_normal(synth.tensor_seed(seed, "limit", big, "W"), (d_out, d_in), 0.02, "bf16", DEV)
+    a = synth.device_normal(synth.tensor_seed(seed, "limit", big, "A"), (E, r, d_in), 1.0 / np.sqrt(d_in), "bf16", DEV)
+    b = synth.device_normal(synth.tensor_seed(seed, "limit", big, "B"), (E, d_out, r), 0.01, "bf16", DEV)
+    sel = [E - 1, 0][:k]
+    idx = torch.tensor(sel, dtype=torch.int32)
+    gate = torch.tensor([0.625, 0.375][:k] if k == 2 else [1.0], dtype=torch.float32)
+    rows = np.arange(d_out) if d_out * d_in <= (1 << 21) else sample_rows(d_out, np.random.default_rng(seed))
+    rows_t = torch.from_numpy(rows).to(DEV)
+    w0 = to64(w[rows_t])
+    a_sel = to64(a[idx.long().to(DEV)])                 # the selected experts only
+    b_sel = to64(b[idx.long().to(DEV)][:, rows_t, :])
+    s = 2.0
+    ref = O.merge(w0, a_sel, b_sel, np.arange(k), gate.numpy().astype(np.float64), s)
+    m = A.AdaModel([(w, None, a, b)], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), s)
+    sync()
+    check_close(w[rows_t], ref, BF16_RTOL, BF16_ATOL, f"merge with {big} at the offset limit")
+    m.destroy()
+    del w, a, b
+    torch.cuda.empty_cache()
 
 
 def test_heavy_cancellation_stays_within_the_folded_gate_bound():
