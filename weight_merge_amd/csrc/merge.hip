@@ -16,7 +16,8 @@
 // the rank-(k*r) product costs 2*k*r flops per weight.  The layout choices serve
 // that stream:
 //   * W goes from HBM to registers and back in a row-major pattern: each load or
-//     store instruction covers whole 256-byte row segments of the tile.  The MFMA's
+//     store instruction covers whole 256-byte row segments of the tile, with the
+//     nontemporal policy (each weight is touched once).  The MFMA's
 //     M index is mapped to W columns and its N index to W rows, so each lane's four
 //     accumulator values are four adjacent columns of one row; the accumulators
 //     reach the W layout through one fp32 pass in LDS.
@@ -66,6 +67,16 @@ __device__ __forceinline__ u32x4 load16(const ADA_GLOBAL unsigned char* base, ui
 }
 __device__ __forceinline__ void store16(ADA_GLOBAL unsigned char* base, uint32_t off, u32x4 v) {
   *reinterpret_cast<ADA_GLOBAL u32x4*>(base + off) = v;
+}
+// The same for the W stream, which a launch touches exactly once: nontemporal loads
+// and stores (the adapter gathers, reused by neighbouring tiles through L2, keep the
+// default policy).  Measured on the 7B stacks: 2.7% faster at k*r = 256, 3% faster
+// for the fused switch, level at k*r = 32; bit-identical.
+__device__ __forceinline__ u32x4 load16_stream(const ADA_GLOBAL unsigned char* base, uint32_t off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const ADA_GLOBAL u32x4*>(base + off));
+}
+__device__ __forceinline__ void store16_stream(ADA_GLOBAL unsigned char* base, uint32_t off, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<ADA_GLOBAL u32x4*>(base + off));
 }
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -287,7 +298,7 @@ merge_bf16_kernel(MergeParams p) {
     const int col = T.col0 + 8 * (v % (BN / 8));
     ok[u] = row < T.d_out && col < T.d_in;
     woff[u] = ok[u] ? 2u * (uint32_t(row) * uint32_t(T.ld) + uint32_t(col)) : 0u;  // out of range: re-read W[0][0..8)
-    wv[u] = load16(src, woff[u]);
+    wv[u] = load16_stream(src, woff[u]);
   }
 
   // 3. active slots, in selection order: index in range and coefficient nonzero
@@ -315,7 +326,7 @@ merge_bf16_kernel(MergeParams p) {
     if (T.src == T.dst) return;
 #pragma unroll
     for (int u = 0; u < NV; ++u)
-      if (ok[u]) store16(dst, woff[u], wv[u]);
+      if (ok[u]) store16_stream(dst, woff[u], wv[u]);
     return;
   }
 
@@ -578,7 +589,7 @@ merge_bf16_kernel(MergeParams p) {
     o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
     o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
     o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
-    store16(dst, woff[u], o);
+    store16_stream(dst, woff[u], o);
   }
 }
 
