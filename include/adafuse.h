@@ -85,8 +85,8 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
  * enqueued merge has completed. */
 void ada_model_destroy(ada_model m);
 
-/* Number of output tiles one short-contraction merge launch of this model covers
- * (64 x 128 tiles for bf16, 64 x 64 for fp32; for measurement); negative status on
+/* Number of output tiles one merge launch of this model covers at k*r <= 32
+ * (32 x 256 tiles for bf16, 64 x 64 for fp32; for measurement); negative status on
  * a bad handle. */
 int64_t ada_model_tiles(ada_model m);
 

@@ -95,6 +95,10 @@ MERGE_CASES = [
     (4, 96, 1, 72, 40, "bf16", True),
     (16, 64, 8, 264, 1032, "bf16", False),
     (3, 64, 2, 8, 64, "bf16", True),
+    # every rank mode of each tile class: k*r <= 32 (32 x 256 tiles) with r = 24, and
+    # k*r <= 64 (64 x 128) with r = 20
+    (5, 24, 1, 72, 520, "bf16", True),
+    (4, 20, 3, 136, 264, "bf16", False),
 ]
 
 
@@ -124,7 +128,7 @@ def test_merge_matches_oracle(E, r, k, d_out, d_in, dt, inplace):
 # operands of fewer than 2^31 elements.  One operand per case sits just under that.
 LIMIT_CASES = [
     # E, r, k, d_out, d_in, operand at the limit
-    (2, 16, 2, 32768, 65528, "W"),   # W: 2,147,221,504 elements (64 x 128 tiles)
+    (2, 16, 2, 32768, 65528, "W"),   # W: 2,147,221,504 elements (32 x 256 tiles)
     (64, 256, 1, 8, 131064, "A"),    # A: 64 x 256 x 131064 = 2,147,352,576 elements (128 x 128 tiles)
     (64, 256, 1, 131064, 8, "B"),    # B: the same count
 ]
@@ -310,10 +314,12 @@ def test_merge_then_unmerge_returns_w(inplace):
         assert torch.equal(w.cpu(), W)
 
 
-@pytest.mark.parametrize("r,E,kp,kc", [(16, 8, 2, 3), (32, 8, 2, 3), (128, 4, 2, 2), (8, 64, 32, 32)])
+@pytest.mark.parametrize("r,E,kp,kc", [(8, 8, 2, 2), (16, 8, 2, 2), (16, 8, 2, 3), (32, 8, 2, 3), (128, 4, 2, 2),
+                                        (8, 64, 32, 32)])
 def test_switch_matches_oracle(r, E, kp, kc):
-    """Undo one selection and apply another in one pass, up to the largest contraction
-    one launch takes ((k_prev + k_cur) * r = 512, in 4 or in 64 slots)."""
+    """Undo one selection and apply another in one pass, in every tile class ((k_prev +
+    k_cur) * r = 32, 64, 80 and up) up to the largest contraction one launch takes
+    (512, in 4 or in 64 slots)."""
     W, Aw, Bw = synth.adapter_bank(43, E, r, 264, 520, "bf16")
     pi, pg = make_selection(E, kp, 64, "bf16", 7)
     ci, cg = make_selection(E, kc, 64, "bf16", 8)

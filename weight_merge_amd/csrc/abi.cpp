@@ -48,7 +48,7 @@ struct ada_model_s {
   int32_t n_proj;
   int32_t device;
   void* dev;          // one allocation holding both tables
-  TileTable tab[2];   // bf16: [0] 64-row tiles (k*r <= 64), [1] 128-row tiles; fp32: both 64 x 64
+  TileTable tab[ada::kTileClasses];  // bf16: one per contraction class (32 x 256, 64 x 128, 128 x 128); fp32: all 64 x 64
 };
 
 namespace {
@@ -57,7 +57,8 @@ bool model_ok(const ada_model_s* m) { return m != nullptr && m->magic == kModelM
 
 int launch_merge_common(ada_model m, const ada::Selection& s0, const ada::Selection& s1,
                         int src_is_out, int kr_max, void* stream) {
-  const TileTable& t = m->tab[m->dtype == ADA_BF16 && kr_max > ada::kLongKR ? 1 : 0];
+  const int cls = m->dtype == ADA_BF16 ? ada::bf16_tile_class(kr_max) : 0;
+  const TileTable& t = m->tab[cls];
   ada::MergeParams p{};
   p.table = t.entries;
   p.lut = t.lut;
@@ -71,7 +72,7 @@ int launch_merge_common(ada_model m, const ada::Selection& s0, const ada::Select
   p.r_shift = (m->r & (m->r - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(m->r)) : -1;
   p.src_is_out = src_is_out;
   p.xcd_remap = 1;
-  p.tile_group = m->dtype == ADA_BF16 && kr_max > ada::kLongKR ? ADA_LONG_TILE_GROUP : 1;
+  p.tile_group = cls == 2 ? ADA_LONG_TILE_GROUP : 1;
   const hipError_t e = ada::launch_merge(p, m->dtype, kr_max, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADA_OK : ADA_EHIP;
 }
@@ -169,23 +170,22 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
         int64_t(E) * r * p.d_out >= kMaxElems)
       return ADA_ESHAPE;
   }
-  HostTable ht[2];
-  for (int t = 0; t < 2; ++t) {
-    const int kr = t == 0 ? ada::kLongKR : ada::kMaxKR;
-    const int tile_r = dtype == ADA_BF16 ? ada::bf16_tile_rows(kr) : ada::kTileF32;
-    const int tile_c = dtype == ADA_BF16 ? ada::bf16_tile_cols(kr) : ada::kTileF32;
+  HostTable ht[ada::kTileClasses];
+  for (int t = 0; t < ada::kTileClasses; ++t) {
+    const int tile_r = dtype == ADA_BF16 ? ada::bf16_tile_rows(t) : ada::kTileF32;
+    const int tile_c = dtype == ADA_BF16 ? ada::bf16_tile_cols(t) : ada::kTileF32;
     if (int st = build_table(projs, n_proj, tile_r, tile_c, ht[t]); st != ADA_OK) return st;
   }
 
-  size_t off[4], bytes = 0;
-  for (int t = 0; t < 2; ++t) {
+  size_t off[2 * ada::kTileClasses], bytes = 0;
+  for (int t = 0; t < ada::kTileClasses; ++t) {
     off[2 * t] = bytes;
     bytes = align16(bytes + ht[t].ent.size() * sizeof(ada::MergeEntry));
     off[2 * t + 1] = bytes;
     bytes = align16(bytes + ht[t].lut.size() * sizeof(int32_t));
   }
   std::vector<unsigned char> host(bytes, 0);
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < ada::kTileClasses; ++t) {
     std::copy_n(reinterpret_cast<const unsigned char*>(ht[t].ent.data()),
                 ht[t].ent.size() * sizeof(ada::MergeEntry), host.data() + off[2 * t]);
     std::copy_n(reinterpret_cast<const unsigned char*>(ht[t].lut.data()), ht[t].lut.size() * sizeof(int32_t),
@@ -211,7 +211,7 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
   m->n_proj = n_proj;
   m->device = device;
   m->dev = dev;
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < ada::kTileClasses; ++t) {
     unsigned char* base = static_cast<unsigned char*>(dev);
     m->tab[t].entries = reinterpret_cast<const ada::MergeEntry*>(base + off[2 * t]);
     m->tab[t].lut = reinterpret_cast<const int32_t*>(base + off[2 * t + 1]);

@@ -7,8 +7,13 @@
 namespace ada {
 
 // Output tile of one merge workgroup (bf16).  A tile shape is RB row blocks and CT
-// column blocks of 16 per wave, with the 4 waves arranged (4 / WGN) x WGN; short
-// contractions (k*r <= kLongKR) and long ones use separate shapes.
+// column blocks of 16 per wave, with the 4 waves arranged (4 / WGN) x WGN.  Three
+// contraction classes use separate shapes: k*r <= kNarrowKR (32 x 256: 512-byte row
+// segments of W per tile row), k*r <= kLongKR (64 x 128: half the A_cat columns to
+// gather per tile) and longer ones (128 x 128).
+#ifndef ADA_NARROW_TILE
+#define ADA_NARROW_TILE 1, 8, 2
+#endif
 #ifndef ADA_SHORT_TILE
 #define ADA_SHORT_TILE 2, 4, 2
 #endif
@@ -20,14 +25,21 @@ struct TileShapeT {
   static constexpr int rb = RB, ct = CT, wgn = WGN;
   static constexpr int rows = 16 * RB * (4 / WGN), cols = 16 * CT * WGN;
 };
+using NarrowTile = TileShapeT<ADA_NARROW_TILE>;
 using ShortTile = TileShapeT<ADA_SHORT_TILE>;
 using LongTile = TileShapeT<ADA_LONG_TILE>;
+constexpr int kNarrowKR = 32;
 constexpr int kLongKR = 64;
-__host__ __device__ constexpr int bf16_tile_rows(int kr_max) {
-  return kr_max <= kLongKR ? ShortTile::rows : LongTile::rows;
+constexpr int kTileClasses = 3;
+// contraction class of a launch whose selections span at most kr_max = k*r terms
+__host__ __device__ constexpr int bf16_tile_class(int kr_max) {
+  return kr_max <= kNarrowKR ? 0 : kr_max <= kLongKR ? 1 : 2;
 }
-__host__ __device__ constexpr int bf16_tile_cols(int kr_max) {
-  return kr_max <= kLongKR ? ShortTile::cols : LongTile::cols;
+__host__ __device__ constexpr int bf16_tile_rows(int cls) {
+  return cls == 0 ? NarrowTile::rows : cls == 1 ? ShortTile::rows : LongTile::rows;
+}
+__host__ __device__ constexpr int bf16_tile_cols(int cls) {
+  return cls == 0 ? NarrowTile::cols : cls == 1 ? ShortTile::cols : LongTile::cols;
 }
 constexpr int kTileF32 = 64;    // 64 x 64 for fp32 storage (VALU path)
 constexpr int kMaxSlots = 128;  // selected adapters per launch (two selections of <= 64)

@@ -9,8 +9,9 @@
 //                                      A_cat = [A_{e_1}; ...; A_{e_k}],
 // with c_j = +scale * g_j to fuse and -scale * g_j to de-fuse.  The pages split the
 // product into GEMM tiles per thread block and hide global-memory latency with a
-// prefetch buffer; here one workgroup owns one 64 x 128 (or 128 x 128) output tile of
-// one projection, found through a work table, so a single grid covers all layers.
+// prefetch buffer; here one workgroup owns one output tile of one projection (32 x 256,
+// 64 x 128 or 128 x 128 by contraction length), found through a work table, so a
+// single grid covers all layers.
 //
 // The merge is bound by HBM: every weight is read once and written once, while
 // the rank-(k*r) product costs 2*k*r flops per weight.  The layout choices serve
@@ -30,9 +31,12 @@
 //     compacting the selection does not wait for the W tile (the vector-memory
 //     counter is in order: the adapter gathers, issued after W, do wait for it, and
 //     the K loop starts once both have arrived).
-//   * Small tiles (64 x 128) keep registers low for short contractions: four waves
-//     per SIMD, so many tiles' W loads are in flight on each CU.  Long contractions
-//     (k*r > 64) use 128 x 128 tiles so each gathered adapter byte serves more weights.
+//   * Small tiles keep registers low for short contractions: four waves per SIMD, so
+//     many tiles' W loads are in flight on each CU.  At k*r <= 32 the tile is 32 x 256
+//     (each tile row a 512-byte run of W; 2.6% faster on the 7B stack than 64 x 128),
+//     up to k*r = 64 it is 64 x 128 (half the A_cat columns to gather: the fused
+//     switch at k*r = 64 runs 8% slower on 32 x 256).  Long contractions use 128 x 128
+//     tiles so each gathered adapter byte serves more weights.
 //   * Workgroup ids are remapped so each XCD walks a contiguous range of tiles,
 //     keeping a projection's adapter rows and columns in that XCD's L2.
 #include "common.h"
@@ -697,13 +701,14 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t
   if (p.total_tiles <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(p.total_tiles)), block(256);
   if (dtype == 1) {
-    // the caller built p's work table for bf16_tile(kr_max)
+    // the caller built p's work table for the tile class of kr_max
     // short contractions loop over 32-deep chunks (a 64-deep chunk costs a wave per
     // SIMD in registers: the fused switch at k*r = 64 ran 30% slower with it)
-    if (kr_max <= kLongKR)
-      launch_bf16<32, ShortTile, false>(p, grid, block, s);
-    else
-      launch_bf16<64, LongTile, true>(p, grid, block, s);
+    switch (bf16_tile_class(kr_max)) {
+      case 0: launch_bf16<32, NarrowTile, false>(p, grid, block, s); break;
+      case 1: launch_bf16<32, ShortTile, false>(p, grid, block, s); break;
+      default: launch_bf16<64, LongTile, true>(p, grid, block, s); break;
+    }
   } else {
     hipLaunchKernelGGL(merge_f32_kernel<32>, grid, block, 0, s, p);
   }
