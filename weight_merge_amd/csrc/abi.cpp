@@ -72,7 +72,10 @@ int launch_merge_common(ada_model m, const ada::Selection& s0, const ada::Select
   p.r_shift = (m->r & (m->r - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(m->r)) : -1;
   p.src_is_out = src_is_out;
   p.xcd_remap = 1;
-  p.tile_group = cls == 2 ? ADA_LONG_TILE_GROUP : 1;
+  // row bands walked in groups down each column block, so consecutive tiles share A_cat
+  // columns and B_cat rows in L2: a gain once k*r > 32 (the 7B fused switch at k*r = 64
+  // runs 2.5% faster), a small loss on 32 x 256 tiles, which walk plain row-major order
+  p.tile_group = cls == 0 ? 1 : ADA_LONG_TILE_GROUP;
   const hipError_t e = ada::launch_merge(p, m->dtype, kr_max, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADA_OK : ADA_EHIP;
 }
