@@ -9,8 +9,9 @@ from weight_merge_amd import synth
 
 # Merged bf16 weights: |W'_gpu - W'_ref| <= 8e-3 |W'_ref| + 1e-4, ref the unrounded
 # fp64 W + delta.  The kernel's arithmetic is RNE(W + sum_t RNE(s g b_t) a_t) with exact
-# products and fp32 sums, so its error is at most 2^-9 |W'| (final rounding) plus
-# 2^-9 sum_t |s g b_t a_t| (gate folded into B in bf16) plus the fp32 accumulation.
+# products and fp32 sums, so its error is at most 2^-8 |W'| (final rounding: half an
+# ulp of bf16's 8 significant bits) plus 2^-8 sum_t |s g b_t a_t| (gate folded into B
+# in bf16) plus the fp32 accumulation.
 # The second term is far below 1e-4 on weight-shaped data (d_in in the thousands, so
 # A ~ N(0, 1/sqrt(d_in)) is small); folded_bound() states the full bound for inputs
 # where it is not.
@@ -46,14 +47,40 @@ def check_close(got: torch.Tensor | np.ndarray, ref: np.ndarray, rtol: float, at
 
 def folded_bound(Aw, Bw, idx, gate, scale: float) -> np.ndarray:
     """Per-element error bound of the bf16 merge's arithmetic beyond the stated
-    tolerance: 2^-8 sum_t |s g b_t a_t| over the selected adapters (twice the worst
-    case of rounding s g B to bf16, for margin)."""
+    tolerance, over the selected adapters' terms sum_t |s g b_t a_t|: 2^-8 of it for
+    rounding s g B to bf16 (half an ulp of 8 significant bits), plus (k r + 2) 2^-23 of
+    it for the fp32 accumulation of k r products (twice the usual gamma, for margin)."""
     A64, B64 = to64(Aw), to64(Bw)
     acc = np.zeros((B64.shape[1], A64.shape[2]))
+    n = 0
     for e, g in zip(np.asarray(idx).tolist(), np.asarray(gate, dtype=np.float64).tolist()):
         if 0 <= e < A64.shape[0] and g != 0.0:
             acc += np.abs(scale * g * B64[e]) @ np.abs(A64[e])
-    return 2.0 ** -8 * acc
+            n += A64.shape[1]
+    return (2.0 ** -8 + (n + 2) * 2.0 ** -23) * acc
+
+
+def folded_gate_model(W, Aw, Bw, slots, scale_sign_pairs=None):
+    """The bf16 merge's arithmetic written out on the CPU (a model of the fused kernel
+    for tighter checks; the oracle stays the exact fp64 method).  The fused kernel
+    concatenates the selected adapters with each gate folded into the up projection
+    ("AdaFuse", Japanese summary page, technical overview 2.2): here each coefficient
+    c = (+-s) g is formed in fp32, c B_e is computed in fp32 and rounded to bf16, and the
+    products with A_e (exact for bf16 operands) are summed in fp64.
+
+    slots: list of (expert, gate, signed scale).  Returns the unrounded fp64 result and
+    |W| + sum_t |b'_t a_t|, the scale of the kernel's fp32 accumulation error."""
+    W64, A64 = to64(W), to64(Aw)
+    B32 = Bw.float()
+    out, mag = W64.copy(), np.abs(W64)
+    for e, g, sc in slots:
+        c = np.float32(sc) * np.float32(g)
+        if not (0 <= e < A64.shape[0]) or c == 0:
+            continue
+        b = (B32[e] * torch.tensor(c, dtype=torch.float32)).to(torch.bfloat16).double().numpy()
+        out = out + b @ A64[e]
+        mag = mag + np.abs(b) @ np.abs(A64[e])
+    return out, mag
 
 
 def min_gap(z) -> float:
