@@ -73,7 +73,8 @@ typedef struct ada_model_s* ada_model;
  * model, in any order).  Builds the per-projection work table the one-launch
  * merge walks ([ja] 2.2: the large product is split into GEMM tiles assigned to
  * thread blocks) and copies it to the current device; this is the only call that
- * allocates (the table: ~64 bytes per projection plus a small tile index).
+ * allocates (one table per contraction class, three in all: ~64 bytes per projection
+ * each plus a small tile index).
  * n_proj >= 1; all projections share E, r and dtype.  On success *out owns the
  * table until ada_model_destroy.  The registered pointers must stay valid, and
  * may not be registered twice in one model.
