@@ -499,8 +499,8 @@ def main():
         return write_traffic(args, PRESETS[args.workload])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the merge needs no communication and this build runs on a "
-              "single MI355X; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the merge needs no communication between GPUs (each merges "
+              "its own shard in one launch), so the figure is one MI355X's; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
