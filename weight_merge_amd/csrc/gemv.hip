@@ -230,34 +230,65 @@ __global__ void __launch_bounds__(256) lora_layer_expand_kernel(LoraLayerParams 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Row pitch (bf16 elements) of a wave's staging window in LDS: 128 k plus 8, so the 16
+// rows of an MFMA fragment read start 16 bytes apart in the bank space.
+constexpr int kBaseLdw = 128 + 8;
+
 // One wave's share of a base tile: contraction steps wave, wave + 4, wave + 8, ...
+// bf16: a step is the tile's 16 rows x 128 k.  W is read row by row (each load
+// instruction covers 4 rows x 256 contiguous bytes, as the decode GEMV streams W)
+// into the wave's own LDS window `stage`, and read back in the MFMA operand layout
+// (16 rows x 16 bytes per instruction): loading the operand layout straight from
+// HBM touches 16 rows x 64 bytes per instruction, and the 7B decode step with 4 to
+// 16 requests ran 10-14% slower that way.  Only
+// the wave itself touches its window, and a wave's LDS accesses run in order, so no
+// barrier is needed.
 template <typename T>
 __device__ __forceinline__ f32x4 base_tile_part(const T* __restrict__ W, int64_t ld, int row0, int d_out,
-                                                const T* __restrict__ X, int d_in, int nb, int wave) {
+                                                const T* __restrict__ X, int d_in, int nb, int wave,
+                                                uint16_t* stage) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, i = lane & 15;
   const T* wrow = W + int64_t(row0 + i < d_out ? row0 + i : 0) * ld;
   const T* xrow = X + int64_t(i < nb ? i : 0) * d_in;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (sizeof(T) == 2) {
-    constexpr int U = 4;  // 32-deep steps in flight per wave
+    constexpr int U = 4;  // 32-deep MFMA steps per 128-k window
+    // row-by-row loads: instruction u covers tile rows 4u .. 4u+3, lane l reading
+    // 16-byte chunk l % 16 of row 4u + l / 16 inside the window
+    const T* lrow[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = row0 + 4 * u + (lane >> 4);
+      lrow[u] = W + int64_t(r < d_out ? r : 0) * ld;
+    }
     for (int k0 = 32 * U * wave; k0 < d_in; k0 += 4 * 32 * U) {
-      uint4 wv[U], xv[U];
+      uint4 wl[U], wv[U], xv[U];
+      const int kl = k0 + 8 * (lane & 15);
+      const bool inl = kl < d_in;  // d_in is a multiple of 8: whole vectors in or out
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint4 w = load_stream(reinterpret_cast<const uint4*>(lrow[u] + (inl ? kl : 0)));
+        wl[u] = inl ? w : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = k0 + 32 * u + 8 * q;
-        const bool in = k < d_in;  // d_in is a multiple of 8: whole vectors in or out
-        const uint4 w = load_stream(reinterpret_cast<const uint4*>(wrow + (in ? k : 0)));
+        const bool in = k < d_in;
         const uint4 x = *reinterpret_cast<const uint4*>(xrow + (in ? k : 0));
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        wv[u] = in ? w : z;
-        xv[u] = in ? x : z;
+        xv[u] = in ? x : make_uint4(0, 0, 0, 0);
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        *reinterpret_cast<uint4*>(stage + (4 * u + (lane >> 4)) * kBaseLdw + 8 * (lane & 15)) = wl[u];
+#pragma unroll
+      for (int u = 0; u < U; ++u) wv[u] = *reinterpret_cast<const uint4*>(stage + i * kBaseLdw + 32 * u + 8 * q);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[u]),
                                                       __builtin_bit_cast(bf16x8_t, xv[u]), acc, 0, 0, 0);
     }
+    (void)wrow;
   } else {
     // fp32: lane (q, i) loads 4 consecutive k; MFMA j takes element j of every lane,
     // i.e. k = k0 + 4 q + j (the same permutation of k on both operands)
@@ -280,6 +311,7 @@ __device__ __forceinline__ f32x4 base_tile_part(const T* __restrict__ W, int64_t
 template <typename T>
 __global__ void __launch_bounds__(256) lora_batch_dot_kernel(LoraLayerParams p) {
   __shared__ f32x4 part[3][64];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4][16 * kBaseLdw];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = blockIdx.x;  // workgroup index
@@ -293,7 +325,8 @@ __global__ void __launch_bounds__(256) lora_batch_dot_kernel(LoraLayerParams p) 
   float* ws = p.ws + P.ws_off;
   if (lw < base_wgs) {
     const int row0 = 16 * lw;
-    f32x4 acc = base_tile_part(static_cast<const T*>(P.w), P.ld, row0, P.d_out, x, P.d_in, p.nb, wave);
+    f32x4 acc = base_tile_part(static_cast<const T*>(P.w), P.ld, row0, P.d_out, x, P.d_in, p.nb, wave,
+                               stage[wave]);
     if (wave > 0) part[wave - 1][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
