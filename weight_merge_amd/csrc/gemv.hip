@@ -144,7 +144,26 @@ __global__ void __launch_bounds__(256) lora_shrink_kernel(const T* __restrict__ 
   if (lane == 0) t[row] = acc;
 }
 
+// Eight consecutive elements of a 16-byte-aligned row as floats.
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    v[2 * h] = __uint_as_float(w[h] << 16);
+    v[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // RNE(y32[i] + sum_j scale * gate[j] * sum_rr B[idx_j][i][rr] t[j*r + rr]) for one row i.
+// When r is a multiple of 8 (rows of B and t then start on 16-byte boundaries: B is
+// 16-byte aligned and every t block starts at a multiple of 4 floats) the row and t are
+// read as 16-byte vectors; the products are summed in the same order either way.
 template <typename T>
 __device__ __forceinline__ float expand_row(const T* __restrict__ B, int E, int r, int d_out, int i,
                                             const int32_t* __restrict__ idx, const float* __restrict__ gate,
@@ -155,8 +174,19 @@ __device__ __forceinline__ float expand_row(const T* __restrict__ B, int E, int 
     const float c = scale * gate[j];
     if (e < 0 || e >= E || c == 0.f) continue;
     const T* br = B + (int64_t(e) * d_out + i) * r;
+    const float* tj = t + j * r;
     float s = 0.f;
-    for (int rr = 0; rr < r; ++rr) s = fmaf(load_elem(br, rr), t[j * r + rr], s);
+    if ((r & 7) == 0) {
+      for (int rr = 0; rr < r; rr += 8) {
+        float bv[8], tv[8];
+        load8(br + rr, bv);
+        load8(tj + rr, tv);
+#pragma unroll
+        for (int h = 0; h < 8; ++h) s = fmaf(bv[h], tv[h], s);
+      }
+    } else {
+      for (int rr = 0; rr < r; ++rr) s = fmaf(load_elem(br, rr), tj[rr], s);
+    }
     acc = fmaf(c, s, acc);
   }
   return acc;
