@@ -125,12 +125,15 @@ def test_merge_matches_oracle(E, r, k, d_out, d_in, dt, inplace):
 
 
 # W and each adapter bank are addressed with 32-bit byte offsets; the library admits
-# operands of fewer than 2^31 elements.  One operand per case sits just under that.
+# operands of fewer than 2^31 elements and dimensions up to 2^22.  One operand or
+# dimension per case sits at its limit.
 LIMIT_CASES = [
     # E, r, k, d_out, d_in, operand at the limit
     (2, 16, 2, 32768, 65528, "W"),   # W: 2,147,221,504 elements (32 x 256 tiles)
     (64, 256, 1, 8, 131064, "A"),    # A: 64 x 256 x 131064 = 2,147,352,576 elements (128 x 128 tiles)
     (64, 256, 1, 131064, 8, "B"),    # B: the same count
+    (1, 8, 1, 8, 4194304, "d_in"),   # the largest dimension accepted (2^22 columns)
+    (1, 8, 1, 4194304, 8, "d_out"),  # and rows
 ]
 
 
