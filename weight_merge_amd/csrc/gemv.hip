@@ -253,7 +253,8 @@ __global__ void __launch_bounds__(256) lora_layer_expand_kernel(LoraLayerParams 
 // MFMA (v_mfma_f32_16x16x32_bf16; fp32: 16x16x4), its 4 waves taking interleaved
 // slices of the contraction and adding their partial tiles in a fixed order through
 // LDS, so each W row is read from HBM once for the whole batch.  Lane l = 16 q + i of
-// a wave supplies W[row i][k .. k+7] and X[request i][k .. k+7] (k = k0 + 8 q) and
+// a wave supplies W[row i][k .. k+7] (bf16: from the wave's LDS window, filled row by
+// row) and X[request i][k .. k+7] (k = k0 + 8 q) and
 // receives D[4 q + c][i] = sum_k W[row 4q + c][k] X[request i][k].  Rows past d_out
 // and requests past nb re-read row / request 0 and are not stored.
 // Grid 2: every request's expand (as ada_lora_layer).
