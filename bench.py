@@ -43,7 +43,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-copy-ceiling", action="store_true", help="skip timing torch's device copy (torch_copy_GBps)")
-    ap.add_argument("--cpu-sample-layers", type=int, default=1)
+    ap.add_argument("--cpu-sample-seconds", type=float, default=10.0,
+                    help="oracle time of the CPU baseline's sample (whole layers, at least one)")
+    ap.add_argument("--cpu-sample-layers", type=int, default=0, help="cap on the sample's layers (0: none)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -193,10 +195,11 @@ def torch_copy_rate(torch, dev, gib=4.0, reps=10):
     return 2 * n * 2 / sec / 1e9
 
 
-def cpu_baseline(cfg, seed, n_layers):
-    """The fp64 NumPy oracle on a bounded sample of the same workload (the first
-    n_layers layers, drawn with the same generator), one step = pregate + merge +
-    unmerge, rated in the benchmark's unit."""
+def cpu_baseline(cfg, seed, target_s, max_layers=0):
+    """The fp64 NumPy oracle on a bounded sample of the same workload: layers 0, 1, ...
+    drawn with the same generator as the GPU stack, one step = pregate + merge +
+    unmerge, until target_s seconds of oracle time (at least one layer; max_layers
+    caps the count when > 0), rated in the benchmark's unit."""
     import numpy as np
 
     from oracle import adafuse as O
@@ -209,28 +212,34 @@ def cpu_baseline(cfg, seed, n_layers):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    sub = scaled(cfg, n_layers)
+    limit = cfg.n_layers if max_layers <= 0 else min(max_layers, cfg.n_layers)
     h, R = synth.router_inputs(cfg, seed)
-    st = synth.make_stack(sub, seed, device="cuda")  # same draws as the GPU stack's first layers
-    host = [[(st.W[l][p].double().cpu().numpy(), st.A[l][p].double().cpu().numpy(),
-              st.B[l][p].double().cpu().numpy()) for p in range(len(sub.projections))] for l in range(n_layers)]
-    del st
     h64, R64 = h.double().numpy(), R.double().numpy()
     t0 = time.perf_counter()
     idx, g = O.pregate(h64, R64, cfg.k, cfg.renorm)
-    for layer in host:
-        for W, A, B in layer:
-            Wm = O.merge(W, A, B, idx, g, cfg.scale)
-            O.unmerge(Wm, A, B, idx, g, cfg.scale)
     sec = time.perf_counter() - t0
-    step_bytes = 2 * sub.merge_bytes() + (cfg.E * cfg.d_model + cfg.d_model) * cfg.elem_bytes
+    done = 0
+    while done < limit and (done == 0 or sec < target_s):
+        W, A, B = synth.draw_layer(cfg, seed, done, device="cuda")  # layer `done` of the GPU stack
+        host = [(w.double().cpu().numpy(), a.double().cpu().numpy(), b.double().cpu().numpy())
+                for w, a, b in zip(W, A, B)]
+        del W, A, B
+        t0 = time.perf_counter()
+        for Wh, Ah, Bh in host:
+            Wm = O.merge(Wh, Ah, Bh, idx, g, cfg.scale)
+            O.unmerge(Wm, Ah, Bh, idx, g, cfg.scale)
+        sec += time.perf_counter() - t0
+        del host
+        done += 1
+    step_bytes = 2 * scaled(cfg, done).merge_bytes() + (cfg.E * cfg.d_model + cfg.d_model) * cfg.elem_bytes
     return {
         "value": round(step_bytes / sec / 1e9, 3),
         "unit": "GB/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"layers 0..{n_layers - 1} of {cfg.n_layers} ({n_layers * len(cfg.projections)} projections): "
-                  f"pregate + merge + unmerge in fp64 NumPy, {sec:.2f} s; inputs copied to host before timing",
+        "sample": f"layers 0..{done - 1} of {cfg.n_layers} ({done * len(cfg.projections)} projections, about "
+                  f"{target_s:g} s of oracle time): pregate + merge + unmerge in fp64 NumPy, {sec:.2f} s; "
+                  f"each layer's inputs copied to host before its timing",
         "seconds": round(sec, 3),
     }
 
@@ -587,7 +596,8 @@ def main():
 
     del model, projs, st
     torch.cuda.empty_cache()
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.seed, args.cpu_sample_layers)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.seed, args.cpu_sample_seconds,
+                                                          args.cpu_sample_layers)
 
     out = {
         "metric": METRIC,

@@ -83,18 +83,24 @@ class Stack:
                 yield l, p, proj
 
 
+def draw_layer(cfg: StackConfig, seed: int, l: int, device=None, weights: bool = True):
+    """W, A and B of every projection of layer l (lists in projection order)."""
+    wl, al, bl = [], [], []
+    for proj in cfg.projections:
+        key = (l, proj.name)
+        wl.append(draw(cfg, seed, key + ("W",), (proj.d_out, proj.d_in), cfg.w_std, device)
+                  if weights else None)
+        al.append(draw(cfg, seed, key + ("A",), (cfg.E, cfg.r, proj.d_in), cfg.a_std(proj.d_in), device))
+        bl.append(draw(cfg, seed, key + ("B",), (cfg.E, proj.d_out, cfg.r), cfg.b_std, device))
+    return wl, al, bl
+
+
 def make_stack(cfg: StackConfig, seed: int, device=None, weights: bool = True) -> Stack:
     """Draw W, A and B for every (layer, projection).  With weights=False only the
     adapter banks are drawn (W left as None), for callers that fill W themselves."""
     W, A, B = [], [], []
     for l in range(cfg.n_layers):
-        wl, al, bl = [], [], []
-        for proj in cfg.projections:
-            key = (l, proj.name)
-            wl.append(draw(cfg, seed, key + ("W",), (proj.d_out, proj.d_in), cfg.w_std, device)
-                      if weights else None)
-            al.append(draw(cfg, seed, key + ("A",), (cfg.E, cfg.r, proj.d_in), cfg.a_std(proj.d_in), device))
-            bl.append(draw(cfg, seed, key + ("B",), (cfg.E, proj.d_out, cfg.r), cfg.b_std, device))
+        wl, al, bl = draw_layer(cfg, seed, l, device, weights)
         W.append(wl)
         A.append(al)
         B.append(bl)
