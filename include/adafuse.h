@@ -76,7 +76,8 @@ typedef struct ada_model_s* ada_model;
  * allocates (one table per contraction class, three in all: ~64 bytes per projection
  * each plus a small tile index).
  * n_proj >= 1; all projections share E, r and dtype.  On success *out owns the
- * table until ada_model_destroy.  The registered pointers must stay valid, and
+ * table until ada_model_destroy.  ada_merge, ada_unmerge and ada_switch return
+ * ADA_EINVAL when another device is current than at creation.  The registered pointers must stay valid, and
  * may not be registered twice in one model.
  */
 int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r,

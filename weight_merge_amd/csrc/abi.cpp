@@ -57,6 +57,10 @@ bool model_ok(const ada_model_s* m) { return m != nullptr && m->magic == kModelM
 
 int launch_merge_common(ada_model m, const ada::Selection& s0, const ada::Selection& s1,
                         int src_is_out, int kr_max, void* stream) {
+  // the work table lives on the device that was current at ada_model_create
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return ADA_EHIP;
+  if (device != m->device) return ADA_EINVAL;
   const int cls = m->dtype == ADA_BF16 ? ada::bf16_tile_class(kr_max) : 0;
   const TileTable& t = m->tab[cls];
   ada::MergeParams p{};
