@@ -17,8 +17,8 @@
 // the rank-(k*r) product costs 2*k*r flops per weight.  The layout choices serve
 // that stream:
 //   * W goes from HBM to registers and back in a row-major pattern: each load or
-//     store instruction covers whole 256-byte row segments of the tile, with the
-//     nontemporal policy (each weight is touched once).  The MFMA's
+//     store instruction covers whole tile rows (256 or 512 contiguous bytes), with
+//     the nontemporal policy (each weight is touched once).  The MFMA's
 //     M index is mapped to W columns and its N index to W rows, so each lane's four
 //     accumulator values are four adjacent columns of one row; the accumulators
 //     reach the W layout through one fp32 pass in LDS.
