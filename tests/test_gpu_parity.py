@@ -88,9 +88,9 @@ MERGE_CASES = [
     (4, 64, 1, 136, 264, "bf16", True),
     (6, 32, 1, 72, 136, "bf16", False),
     (5, 128, 3, 200, 392, "bf16", True),
-    # long contractions with r a multiple of 32 (copied into an LDS ring): fewer
-    # chunks than the prefetch depth, several chunks per slot with a tile narrower than
-    # one column block, a ring that wraps many times, and a matrix smaller than a tile
+    # long contractions (128 x 128 tiles, 64-deep chunks): two slots per chunk (r = 32),
+    # a slot ending inside a half-empty last chunk on a matrix narrower than a tile
+    # (r = 96), eight one-slot chunks, and a matrix smaller than a tile
     (8, 32, 3, 136, 264, "bf16", False),
     (4, 96, 1, 72, 40, "bf16", True),
     (16, 64, 8, 264, 1032, "bf16", False),
