@@ -78,7 +78,8 @@ typedef struct ada_model_s* ada_model;
  * n_proj >= 1; all projections share E, r and dtype.  On success *out owns the
  * table until ada_model_destroy.  ada_merge, ada_unmerge and ada_switch return
  * ADA_EINVAL when another device is current than at creation.  The registered pointers must stay valid, and
- * may not be registered twice in one model.
+ * may not be registered twice in one model.  An out-of-place w_out must not overlap
+ * any registered w, w_out, a or b (the launch reads and writes all tiles at once).
  */
 int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r,
                      int32_t dtype, ada_model* out);
