@@ -512,6 +512,44 @@ def test_live_model_rejects_bad_selections():
         A.ada_merge(m, idx, gate, 2.0)
 
 
+def test_binding_rejects_tensors_the_c_calls_would_misread():
+    """The binding hands the C calls bare pointers, so a strided view, a wrong shape or
+    a wrong dtype must be refused before any launch; nothing below reaches the GPU."""
+    E, r, k, d_out, d_in = 4, 8, 2, 16, 24
+    W, Aw, Bw = synth.adapter_bank(72, E, r, d_out, d_in, "bf16")
+    w, a, b = W.to(DEV), Aw.to(DEV), Bw.to(DEV)
+    m = A.AdaModel([(w, None, a, b)], E, r)
+    idx = torch.tensor([0, 1, 2, 3], dtype=torch.int32, device=DEV)
+    gate = torch.full((4,), 0.25, dtype=torch.float32, device=DEV)
+    before = w.clone()
+    with pytest.raises(ValueError):
+        A.ada_merge(m, idx[::2], gate[:2], 2.0)  # strided idx
+    with pytest.raises(ValueError):
+        A.ada_merge(m, idx.view(2, 2), gate.view(2, 2), 2.0)  # not one-dimensional
+    with pytest.raises(TypeError):
+        A.ada_merge(m, idx.long(), gate, 2.0)
+    x = torch.ones(d_in, dtype=torch.bfloat16, device=DEV)
+    for y in (torch.empty(d_out + 8, dtype=torch.bfloat16, device=DEV),
+              torch.empty(2 * d_out, dtype=torch.bfloat16, device=DEV)[::2],
+              torch.empty(d_out, dtype=torch.float32, device=DEV)):
+        with pytest.raises(ValueError):
+            A.ada_decode_gemv(w, x, y)
+        with pytest.raises(ValueError):
+            A.ada_lora_apply(w, a, b, idx[:k], gate[:k], 2.0, x, y)
+    with pytest.raises(ValueError):
+        A.ada_lora_apply(w, a, b, idx[:k], gate[:k], 2.0, x[:8])
+    with pytest.raises(TypeError):
+        A.ada_lora_apply(w, a, b.float(), idx[:k], gate[:k], 2.0, x)
+    y = torch.empty(d_out, dtype=torch.float32, device=DEV)
+    with pytest.raises(TypeError):
+        A.ada_lora_layer([(w, a, b, x, y)], idx[:k], gate[:k], 2.0)
+    with pytest.raises(ValueError):
+        A.ada_pregate(x, w[:, :d_in].contiguous()[:E], k, idx_out=torch.empty(k, dtype=torch.int64, device=DEV))
+    sync()
+    assert torch.equal(w, before)
+    m.destroy()
+
+
 # ---------------------------------------------------------------- fused unmerged layer (comparator)
 
 

@@ -55,6 +55,13 @@ def _contig(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t: torch.Tensor, shape, dtype, name: str):
+    """A caller-provided output: the C call writes numel(shape) contiguous elements."""
+    _contig(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 def ada_pregate(h: torch.Tensor, router: torch.Tensor, k: int, renorm: bool = True,
                 idx_out: torch.Tensor | None = None, gate_out: torch.Tensor | None = None,
                 stream=None):
@@ -69,6 +76,8 @@ def ada_pregate(h: torch.Tensor, router: torch.Tensor, k: int, renorm: bool = Tr
         idx_out = torch.empty(k, dtype=torch.int32, device=h.device)
     if gate_out is None:
         gate_out = torch.empty(k, dtype=torch.float32, device=h.device)
+    _out(idx_out, (k,), torch.int32, "idx_out")
+    _out(gate_out, (k,), torch.float32, "gate_out")
     st = _lib.load().ada_pregate(_dev(h, "h"), _dev(router, "router"), d, E, k, _dtype(h), int(bool(renorm)),
                                  _dev(idx_out, "idx_out"), _dev(gate_out, "gate_out"), _stream(stream))
     _check(st, "ada_pregate")
@@ -139,8 +148,10 @@ class AdaModel:
 def _sel(idx: torch.Tensor, gate: torch.Tensor):
     if idx.dtype != torch.int32 or gate.dtype != torch.float32:
         raise TypeError("idx must be int32 and gate float32")
-    if idx.numel() != gate.numel():
-        raise ValueError("idx and gate must have the same length")
+    if idx.dim() != 1 or gate.dim() != 1 or idx.numel() != gate.numel():
+        raise ValueError("idx and gate must be one-dimensional and of the same length")
+    _contig(idx, "idx")
+    _contig(gate, "gate")
     return _dev(idx, "idx"), _dev(gate, "gate"), idx.numel()
 
 
@@ -174,6 +185,7 @@ def ada_decode_gemv(w: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = N
         raise ValueError("x must be [d_in] with w's dtype")
     if y is None:
         y = torch.empty(d_out, dtype=w.dtype, device=w.device)
+    _out(y, (d_out,), w.dtype, "y")
     st = _lib.load().ada_decode_gemv(_dev(w, "w"), d_out, d_in, w.stride(0), _dev(x, "x"), _dev(y, "y"),
                                      _dtype(w), _stream(stream))
     _check(st, "ada_decode_gemv")
@@ -206,11 +218,21 @@ def ada_lora_apply(w, a, b, idx, gate, scale: float, x, y=None, workspace=None, 
     d_out, d_in = w.shape
     E, r, _ = a.shape
     pi, pg, k = _sel(idx, gate)
+    if w.stride(1) != 1:
+        raise ValueError("w must have unit column stride")
+    for t, n in ((a, "a"), (b, "b"), (x, "x")):
+        _contig(t, n)
+    if a.shape != (E, r, d_in) or b.shape != (E, d_out, r) or x.shape != (d_in,):
+        raise ValueError("projection shapes do not match")
+    if a.dtype != w.dtype or b.dtype != w.dtype or x.dtype != w.dtype:
+        raise TypeError("all tensors share one dtype")
     if y is None:
         y = torch.empty(d_out, dtype=w.dtype, device=w.device)
+    _out(y, (d_out,), w.dtype, "y")
     need = (d_out + k * r) * 4
     if workspace is None:
         workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=w.device)
+    _contig(workspace, "workspace")
     st = _lib.load().ada_lora_apply(_dev(w, "w"), d_out, d_in, w.stride(0), _dev(a, "a"), _dev(b, "b"),
                                     E, r, pi, pg, k, float(scale), _dev(x, "x"), _dev(y, "y"),
                                     _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
@@ -245,11 +267,14 @@ def ada_lora_layer(projs, idx, gate, scale: float, workspace=None, stream=None):
             _contig(t, n)
         if a.shape != (E, r, d_in) or b.shape != (E, d_out, r) or x.shape != (d_in,) or y.shape != (d_out,):
             raise ValueError("projection shapes do not match")
+        if any(t.dtype != w0.dtype for t in (w, a, b, x, y)):
+            raise TypeError("all tensors share one dtype")
         arr[i] = AdaLoraProj(_dev(w, "w"), _dev(a, "a"), _dev(b, "b"), _dev(x, "x"), _dev(y, "y"), d_out, d_in,
                              w.stride(0))
     need = lora_layer_workspace_elems([p[0].shape[0] for p in projs], k, r)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.float32, device=w0.device)
+    _contig(workspace, "workspace")
     st = _lib.load().ada_lora_layer(arr, len(projs), E, r, pi, pg, k, float(scale), _dev(workspace, "workspace"),
                                     workspace.numel() * workspace.element_size(), _dtype(w0), _stream(stream))
     _check(st, "ada_lora_layer")
@@ -288,11 +313,14 @@ def ada_lora_batch(projs, idx, gate, scale: float, workspace=None, stream=None):
             _contig(t, n)
         if a.shape != (E, r, d_in) or b.shape != (E, d_out, r) or x.shape != (nb, d_in) or y.shape != (nb, d_out):
             raise ValueError("projection shapes do not match")
+        if any(t.dtype != w0.dtype for t in (w, a, b, x, y)):
+            raise TypeError("all tensors share one dtype")
         arr[i] = AdaLoraProj(_dev(w, "w"), _dev(a, "a"), _dev(b, "b"), _dev(x, "x"), _dev(y, "y"), d_out, d_in,
                              w.stride(0))
     need = lora_batch_workspace_elems([p[0].shape[0] for p in projs], nb, k, r)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.float32, device=w0.device)
+    _contig(workspace, "workspace")
     st = _lib.load().ada_lora_batch(arr, len(projs), nb, E, r, _dev(idx, "idx"), _dev(gate, "gate"), k,
                                     float(scale), _dev(workspace, "workspace"),
                                     workspace.numel() * workspace.element_size(), _dtype(w0), _stream(stream))
