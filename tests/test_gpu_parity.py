@@ -229,10 +229,11 @@ def test_merge_is_the_folded_gate_arithmetic(E, r, k, d_out, d_in):
     m2.destroy()
 
 
-def test_stack_of_mixed_shapes_in_one_launch():
+@pytest.mark.parametrize("E,r,k", [(8, 16, 2), (8, 16, 4), (16, 64, 4)])  # each tile class
+def test_stack_of_mixed_shapes_in_one_launch(E, r, k):
     """Several projections of different shapes in one model (one launch): every
     projection gets its own adapters and the same selection."""
-    E, r, k, dt = 8, 16, 2, "bf16"
+    dt = "bf16"
     shapes = [(256, 256), (64, 256), (688, 256), (256, 688), (8, 8), (136, 1000)] * 2
     banks = [synth.adapter_bank(100 + i, E, r, do, di, dt) for i, (do, di) in enumerate(shapes)]
     idx, gate = make_selection(E, k, 256, dt, 9)
@@ -245,9 +246,10 @@ def test_stack_of_mixed_shapes_in_one_launch():
         check_close(w, ref, *tol(torch.bfloat16), f"merge {tuple(W.shape)}")
 
 
-def test_row_strided_weights():
-    """W with a row stride larger than d_in (a column slice of a wider matrix)."""
-    E, r, k = 8, 16, 2
+@pytest.mark.parametrize("E,r,k", [(8, 16, 2), (8, 16, 4), (16, 64, 4)])  # each tile class
+@pytest.mark.parametrize("inplace", [True, False])
+def test_row_strided_weights(E, r, k, inplace):
+    """W (and W') with a row stride larger than d_in (column slices of wider matrices)."""
     big, Aw, Bw = synth.adapter_bank(21, E, r, 264, 512, "bf16")
     W = big[:, :392]  # ld 512, d_in 392
     Aw = Aw[:, :, :392].contiguous()
@@ -255,11 +257,17 @@ def test_row_strided_weights():
     ref = O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64), 2.0)
     wbig = big.to(DEV)
     w = wbig[:, :392]
-    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    obig = torch.full_like(wbig, float("nan"))
+    out = None if inplace else obig[:, :392]
+    m = A.AdaModel([(w, out, Aw.to(DEV), Bw.to(DEV))], E, r)
     A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
     sync()
-    check_close(w, ref, *tol(torch.bfloat16), "strided merge")
+    check_close(w if inplace else out, ref, *tol(torch.bfloat16), f"strided merge, k*r = {k * r}")
     assert torch.equal(wbig[:, 392:].cpu(), big[:, 392:]), "columns past d_in must stay untouched"
+    if not inplace:
+        assert torch.equal(wbig.cpu(), big), "an out-of-place merge must not write W"
+        assert torch.isnan(obig[:, 392:]).all(), "columns past d_in of W' must stay untouched"
+    m.destroy()
 
 
 @pytest.mark.parametrize("dt,r", [("bf16", 16), ("bf16", 64), ("fp32", 16)])
