@@ -79,3 +79,37 @@ def test_llama70b_tp8_shard_stack():
     # and the 1024-column o projection of layer 0
     frac = run_stack(LLAMA70B_TP8_E8R16K2, 4000, lambda l, p, proj: l == 0 and proj.name in ("k", "v", "o"))
     assert frac > 0.8
+
+
+def test_llama7b_e8r16k2_fused_switch():
+    """The fused switch over the whole 7B-shaped stack in one launch (undo one selection
+    and apply another with one read and one write of every weight), from the pristine
+    weights: sampled rows of every projection, and every element of layer 0, against
+    the oracle's W - delta(prev) + delta(cur)."""
+    cfg = LLAMA7B_E8R16K2
+    h1, R1, seed = gapped_stack_router(cfg, 6000)
+    h2, R2, _ = gapped_stack_router(cfg, 7000)
+    sels = []
+    for h, R in ((h1, R1), (h2, R2)):
+        i, g = O.pregate(to64(h), to64(R), cfg.k, cfg.renorm)
+        g32 = np.asarray(g, dtype=np.float32)  # the values the kernel reads
+        sels.append((np.asarray(i), g32.astype(np.float64),
+                     torch.tensor(i, dtype=torch.int32, device=DEV), torch.from_numpy(g32).to(DEV)))
+    assert sels[0][0].tolist() != sels[1][0].tolist(), "the two selections must differ"
+    st = synth.make_stack(cfg, seed, device=DEV)
+    rng = np.random.default_rng(seed)
+    keep = []
+    for l, p, proj in st.items():
+        rows = np.arange(proj.d_out) if l == 0 else sample_rows(proj.d_out, rng)
+        keep.append((l, p, rows, st.W[l][p][torch.from_numpy(rows).to(DEV)].cpu()))
+    model = A.AdaModel([(st.W[l][p], None, st.A[l][p], st.B[l][p]) for l, p, _ in st.items()], cfg.E, cfg.r)
+    A.ada_switch(model, (sels[0][2], sels[0][3]), (sels[1][2], sels[1][3]), cfg.scale)
+    torch.cuda.synchronize()
+    for l, p, rows, w0 in keep:
+        rows_t = torch.from_numpy(rows).to(DEV)
+        ref = O.switch(to64(w0), to64(st.A[l][p]), to64(st.B[l][p][:, rows_t, :]), sels[0][:2], sels[1][:2],
+                       cfg.scale)
+        check_close(st.W[l][p][rows_t], ref, BF16_RTOL, BF16_ATOL, f"switch layer {l} proj {cfg.projections[p].name}")
+    model.destroy()
+    del st
+    torch.cuda.empty_cache()
