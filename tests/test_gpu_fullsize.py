@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (BF16_ATOL, BF16_RTOL, GATE_ATOL, GATE_RTOL, check_close, gapped_stack_router, sample_rows,
+from helpers import (BF16_ATOL, BF16_RTOL, GATE_ATOL, GATE_RTOL, check_close, gapped_router, gapped_stack_router,
+                     oracle_selection, sample_rows,
                      to64)
 from oracle import adafuse as O
 from weight_merge_amd import api as A
@@ -113,3 +114,45 @@ def test_llama7b_e8r16k2_fused_switch():
     model.destroy()
     del st
     torch.cuda.empty_cache()
+
+
+def test_unmerged_paths_at_7b_layer_shapes():
+    """One decoder layer of the 7B-shaped stack (q, k, v, o 4096 x 4096; gate, up
+    11008 x 4096; down 4096 x 11008) through the unmerged routed paths at full shape,
+    in the decode groups ({q, k, v}, {o}, {gate, up}, {down}): the batched path with
+    16 requests, each with its own selection, and the single-request layer path;
+    every output within the GEMV bound of the oracle's routed forward."""
+    E, r, k, nb = 8, 16, 2, 16
+    shapes = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
+              "gate": (11008, 4096), "up": (11008, 4096), "down": (4096, 11008)}
+    groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+    banks = {n: synth.adapter_bank(800 + i, E, r, do, di, "bf16") for i, (n, (do, di)) in enumerate(shapes.items())}
+    xs = {n: synth.host_normal(synth.tensor_seed(900 + i, di), (nb, di), 1.0, "bf16")
+          for i, (n, (_, di)) in enumerate(shapes.items())}
+    sels = []
+    for b in range(nb):
+        h, R, _ = gapped_router(E, 64, "bf16", 60 + 7 * b)
+        sels.append(oracle_selection(h, R, k))
+    idx = torch.stack([s[0] for s in sels]).contiguous()
+    gate = torch.stack([s[1] for s in sels]).contiguous()
+    assert len({tuple(row) for row in idx.tolist()}) > 1, "the batch must mix selections"
+    dev = {n: tuple(t.to(DEV) for t in banks[n]) for n in shapes}
+    xd = {n: xs[n].to(DEV) for n in shapes}
+    ys = {n: torch.full((nb, shapes[n][0]), float("nan"), dtype=torch.bfloat16, device=DEV) for n in shapes}
+    y1 = {n: torch.full((shapes[n][0],), float("nan"), dtype=torch.bfloat16, device=DEV) for n in shapes}
+    didx, dgate = idx.to(DEV), gate.to(DEV)
+    for gr in groups:
+        A.ada_lora_batch([(dev[n][0], dev[n][1], dev[n][2], xd[n], ys[n]) for n in gr], didx, dgate, 2.0)
+        A.ada_lora_layer([(dev[n][0], dev[n][1], dev[n][2], xd[n][0].contiguous(), y1[n]) for n in gr],
+                         didx[0].contiguous(), dgate[0].contiguous(), 2.0)
+    torch.cuda.synchronize()
+    for n, (W, Aw, Bw) in banks.items():
+        W64, A64, B64 = to64(W), to64(Aw), to64(Bw)
+        got = to64(ys[n])
+        for b in range(nb):
+            x64 = to64(xs[n][b])
+            ref = O.routed_lora_forward(W64, A64, B64, idx[b].numpy(), gate[b].numpy().astype(np.float64), 2.0, x64)
+            bound = 8e-3 * np.abs(ref) + 1e-4 * (np.abs(W64) @ np.abs(x64))
+            assert np.all(np.abs(got[b] - ref) <= bound), (n, b, float(np.max(np.abs(got[b] - ref) / bound)))
+            if b == 0:
+                assert np.all(np.abs(to64(y1[n]) - ref) <= bound), (n, "single request")
