@@ -646,3 +646,131 @@ def test_decode_gemv_layer_is_the_per_projection_gemv(dt):
         W64, x64 = to64(W), to64(x)
         ref = O.gemv(W64, x64)
         assert np.all(np.abs(to64(y) - ref) <= gemv_bound(W64, x64, ref, dt))
+
+
+# ---------------------------------------------------------------- graph capture
+
+
+def test_captured_decode_paths_replay_like_eager():
+    """The decode-time paths as the benchmark captures them in HIP graphs (merged-weight
+    GEMVs in groups, the routed baseline with its per-layer pre-gating, the fused
+    unmerged layer path and the batched path): every replay, with unrelated eager work
+    and synchronisation between replays, gives bit-identical outputs to the eager run."""
+    E, r, k, nb, L = 8, 16, 2, 4, 2
+    shapes = [(264, 520), (136, 264), (520, 136)]
+    groups = [[0, 1], [2]]
+    banks = [[tuple(t.to(DEV) for t in synth.adapter_bank(1000 + 10 * l + i, E, r, do, di, "bf16"))
+              for i, (do, di) in enumerate(shapes)] for l in range(L)]
+    xs = [synth.host_normal(synth.tensor_seed(1100 + i, di), (nb, di), 1.0, "bf16").to(DEV)
+          for i, (_, di) in enumerate(shapes)]
+    h, R, _ = gapped_router(E, 256, "bf16", 5)
+    h, R = h.to(DEV), R.to(DEV)
+    idx, gate = A.ada_pregate(h, R, k)
+    bidx = torch.stack([oracle_selection(*gapped_router(E, 64, "bf16", 70 + 7 * b)[:2], k)[0] for b in range(nb)])
+    bgate = torch.stack([oracle_selection(*gapped_router(E, 64, "bf16", 70 + 7 * b)[:2], k)[1] for b in range(nb)])
+    bidx, bgate = bidx.contiguous().to(DEV), bgate.contiguous().to(DEV)
+    lidx = [torch.empty(k, dtype=torch.int32, device=DEV) for _ in range(L)]
+    lgate = [torch.empty(k, dtype=torch.float32, device=DEV) for _ in range(L)]
+    ys = {name: [[torch.empty(nb, do, dtype=torch.bfloat16, device=DEV) for do, _ in shapes] for _ in range(L)]
+          for name in ("merged", "baseline", "fused", "batch")}
+    ws_apply = [[torch.empty(A.lora_layer_workspace_elems([do], k, r), dtype=torch.float32, device=DEV)
+                 for do, _ in shapes] for _ in range(L)]
+    ws_layer = [[torch.empty(A.lora_layer_workspace_elems([shapes[p][0] for p in g], k, r), dtype=torch.float32,
+                             device=DEV) for g in groups] for _ in range(L)]
+    ws_batch = [[torch.empty(A.lora_batch_workspace_elems([shapes[p][0] for p in g], nb, k, r),
+                             dtype=torch.float32, device=DEV) for g in groups] for _ in range(L)]
+
+    def merged():
+        for l in range(L):
+            for g in groups:
+                A.ada_decode_gemv_layer([(banks[l][p][0], xs[p][0], ys["merged"][l][p][0]) for p in g])
+
+    def baseline():
+        for l in range(L):
+            A.ada_pregate(h, R, k, True, lidx[l], lgate[l])
+            for p in range(len(shapes)):
+                w, a, b = banks[l][p]
+                A.ada_lora_apply(w, a, b, lidx[l], lgate[l], 2.0, xs[p][0], ys["baseline"][l][p][0], ws_apply[l][p])
+
+    def fused():
+        for l in range(L):
+            A.ada_pregate(h, R, k, True, lidx[l], lgate[l])
+            for gi, g in enumerate(groups):
+                A.ada_lora_layer([(*banks[l][p], xs[p][0], ys["fused"][l][p][0]) for p in g], lidx[l], lgate[l],
+                                 2.0, ws_layer[l][gi])
+
+    def batch():
+        for l in range(L):
+            for gi, g in enumerate(groups):
+                A.ada_lora_batch([(*banks[l][p], xs[p], ys["batch"][l][p]) for p in g], bidx, bgate, 2.0,
+                                 ws_batch[l][gi])
+
+    paths = {"merged": merged, "baseline": baseline, "fused": fused, "batch": batch}
+    eager = {}
+    for name, fn in paths.items():
+        fn()
+        sync()
+        eager[name] = [[y.clone() for y in row] for row in ys[name]]
+    graphs = {}
+    for name, fn in paths.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    other = torch.randn(1 << 20, device=DEV)
+    for rep in range(3):
+        for name, g in graphs.items():
+            for row in ys[name]:
+                for y in row:
+                    y.fill_(float("nan"))
+            other.mul_(1.0001).add_(0.5)  # unrelated eager work between replays
+            sync()
+            g.replay()
+            sync()
+            for l in range(L):
+                for p in range(len(shapes)):
+                    got, want = ys[name][l][p], eager[name][l][p]
+                    rows = slice(None) if name == "batch" else slice(0, 1)
+                    assert torch.equal(got[rows].view(torch.int16), want[rows].view(torch.int16)), (name, rep, l, p)
+
+
+@pytest.mark.parametrize("E,r,k", [(8, 16, 2), (8, 16, 4), (16, 64, 4)])  # each tile class
+def test_captured_pregate_and_merge_replay_like_eager(E, r, k):
+    """Pre-gating plus an out-of-place merge captured in one HIP graph: each replay,
+    with unrelated eager work and synchronisation between replays, rewrites W' from the
+    untouched W bit-identically to the eager run."""
+    shapes = [(264, 520), (136, 264)]
+    banks = [tuple(t.to(DEV) for t in synth.adapter_bank(1200 + i, E, r, do, di, "bf16"))
+             for i, (do, di) in enumerate(shapes)]
+    outs = [torch.empty_like(w) for w, _, _ in banks]
+    model = A.AdaModel([(w, o, a, b) for (w, a, b), o in zip(banks, outs)], E, r)
+    h, R, _ = gapped_router(E, 256, "bf16", 11)
+    h, R = h.to(DEV), R.to(DEV)
+    idx = torch.empty(k, dtype=torch.int32, device=DEV)
+    gate = torch.empty(k, dtype=torch.float32, device=DEV)
+
+    def step():
+        A.ada_pregate(h, R, k, True, idx, gate)
+        A.ada_merge(model, idx, gate, 2.0)
+
+    step()
+    sync()
+    eager = [o.clone() for o in outs]
+    w_before = [w.clone() for w, _, _ in banks]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = torch.randn(1 << 20, device=DEV)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        idx.fill_(-1)
+        other.mul_(1.0001).add_(0.5)
+        sync()
+        g.replay()
+        sync()
+        for o, want in zip(outs, eager):
+            assert torch.equal(o.view(torch.int16), want.view(torch.int16)), rep
+    for (w, _, _), w0 in zip(banks, w_before):
+        assert torch.equal(w.view(torch.int16), w0.view(torch.int16))
+    model.destroy()
