@@ -70,7 +70,23 @@ __global__ void __launch_bounds__(1024) pregate_kernel(const T* __restrict__ h,
   for (int e = wave; e < E; e += nwave) {
     const uint4* rv = reinterpret_cast<const uint4*>(R + int64_t(e) * d);
     float acc = 0.f;
-    for (int v = lane; v < nvec; v += 64) dot8(rv[v], hv[v], acc, T());
+    // batches of U vectors per lane, all loads issued before any is used (one round
+    // trip per batch instead of one per vector); past the row end a lane re-reads
+    // vector 0 and multiplies it by zeros
+    constexpr int U = 8;
+    for (int v0 = 0; v0 < nvec; v0 += 64 * U) {
+      uint4 rr[U], hh[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + lane + 64 * u;
+        const bool in = v < nvec;
+        rr[u] = rv[in ? v : 0];
+        const uint4 hx = hv[in ? v : 0];
+        hh[u] = in ? hx : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) dot8(rr[u], hh[u], acc, T());
+    }
     acc = wave_sum(acc);
     if (lane == 0) z[e] = acc;
   }
