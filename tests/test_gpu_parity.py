@@ -124,6 +124,50 @@ def test_merge_matches_oracle(E, r, k, d_out, d_in, dt, inplace):
         assert torch.equal(w.cpu(), W), "out-of-place merge must not write W"
 
 
+def _random_merge_cases(n: int = 32, seed: int = 20261203):
+    """Seeded draws over the whole admitted range: E up to 64, ranks from 1 to 256
+    (every rank mode), k up to min(E, 512 / r) (every tile class), ragged shapes, both
+    storage types, in and out of place."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        E = int(rng.integers(1, 65))
+        r = int(rng.choice([1, 3, 5, 8, 12, 16, 20, 24, 32, 40, 48, 64, 96, 128, 256]))
+        kmax = min(E, 512 // r)
+        k = int(rng.integers(1, kmax + 1))
+        d_out, d_in = 8 * int(rng.integers(1, 90)), 8 * int(rng.integers(1, 90))
+        dt = "bf16" if rng.random() < 0.75 else "fp32"
+        cases.append((E, r, k, d_out, d_in, dt, bool(rng.random() < 0.5)))
+    return cases
+
+
+@pytest.mark.parametrize("E,r,k,d_out,d_in,dt,inplace", _random_merge_cases())
+def test_merge_matches_oracle_on_random_shapes(E, r, k, d_out, d_in, dt, inplace):
+    """The stated tolerance, plus the kernel's own rounding of the folded gate (bf16)
+    and its fp32 accumulation over k r terms, both relative to sum_t |s g b_t a_t|:
+    small d_in makes A large, and weights that cancel then feel them."""
+    W, Aw, Bw = synth.adapter_bank(17 + d_out + d_in, E, r, d_out, d_in, dt)
+    idx, gate = make_selection(E, k, 64, dt, 5)
+    g64 = gate.numpy().astype(np.float64)
+    ref = O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), g64, 2.0)
+    w = W.to(DEV)
+    out = None if inplace else torch.full_like(w, float("nan"))
+    m = A.AdaModel([(w, out, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_merge(m, idx.to(DEV), gate.to(DEV), 2.0)
+    sync()
+    got = to64(w if inplace else out)
+    rtol, atol = tol(TD[dt])
+    extra = folded_bound(Aw, Bw, idx.numpy(), g64, 2.0)
+    if dt == "fp32":  # no bf16 folding: keep the accumulation part only
+        extra = extra * ((k * r + 2) * 2.0 ** -23 / (2.0 ** -8 + (k * r + 2) * 2.0 ** -23))
+    bound = rtol * np.abs(ref) + atol + extra
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), (float(np.max(err / bound)), int((err > bound).sum()))
+    if not inplace:
+        assert torch.equal(w.cpu(), W), "out-of-place merge must not write W"
+    m.destroy()
+
+
 # W and each adapter bank are addressed with 32-bit byte offsets; the library admits
 # operands of fewer than 2^31 elements and dimensions up to 2^22.  One operand or
 # dimension per case sits at its limit.
