@@ -432,6 +432,40 @@ def test_switch_matches_oracle(r, E, kp, kc):
     check_close(w, ref, *tol(torch.bfloat16), "switch")
 
 
+def _random_switch_cases(n: int = 12, seed: int = 20261204):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        E = int(rng.integers(2, 65))
+        r = int(rng.choice([1, 5, 8, 12, 16, 24, 32, 48, 64, 128]))
+        kp = int(rng.integers(1, min(E, max(1, 512 // r - 1)) + 1))
+        kc = int(rng.integers(1, min(E, 512 // r - kp) + 1)) if 512 // r - kp >= 1 else 0
+        if kc < 1:
+            continue
+        cases.append((E, r, kp, kc, 8 * int(rng.integers(1, 60)), 8 * int(rng.integers(1, 60))))
+    return cases
+
+
+@pytest.mark.parametrize("E,r,kp,kc,d_out,d_in", _random_switch_cases())
+def test_switch_matches_oracle_on_random_shapes(E, r, kp, kc, d_out, d_in):
+    """Seeded draws of the fused switch: (k_prev + k_cur) r up to 512, ragged shapes;
+    stated tolerance plus the folding and accumulation allowance of both selections."""
+    W, Aw, Bw = synth.adapter_bank(29 + d_out + d_in, E, r, d_out, d_in, "bf16")
+    pi, pg = make_selection(E, kp, 64, "bf16", 11)
+    ci, cg = make_selection(E, kc, 64, "bf16", 13)
+    p64, c64 = pg.numpy().astype(np.float64), cg.numpy().astype(np.float64)
+    ref = O.switch(to64(W), to64(Aw), to64(Bw), (pi.numpy(), p64), (ci.numpy(), c64), 2.0)
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    A.ada_switch(m, (pi.to(DEV), pg.to(DEV)), (ci.to(DEV), cg.to(DEV)), 2.0)
+    sync()
+    extra = folded_bound(Aw, Bw, pi.numpy(), p64, 2.0) + folded_bound(Aw, Bw, ci.numpy(), c64, 2.0)
+    err = np.abs(to64(w) - ref)
+    bound = BF16_RTOL * np.abs(ref) + BF16_ATOL + extra
+    assert (err <= bound).all(), (float(np.max(err / bound)), int((err > bound).sum()))
+    m.destroy()
+
+
 # ---------------------------------------------------------------- invariants
 
 
