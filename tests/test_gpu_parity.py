@@ -47,6 +47,28 @@ def test_pregate_matches_oracle(E, k, d, dt, renorm):
         check_close(gate, rg, GATE_RTOL, GATE_ATOL, "gates")
 
 
+def _random_pregate_cases(n: int = 16, seed: int = 20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.integers(1, 65))
+        out.append((E, int(rng.integers(1, E + 1)), 8 * int(rng.integers(1, 1100)),
+                    "bf16" if rng.random() < 0.7 else "fp32", bool(rng.random() < 0.8)))
+    return out
+
+
+@pytest.mark.parametrize("E,k,d,dt,renorm", _random_pregate_cases())
+def test_pregate_matches_oracle_on_random_shapes(E, k, d, dt, renorm):
+    """Seeded draws of (E, k, d, dtype, renorm), d up to 8792 (ragged batches of the
+    row loads): indices bit-exact, gates within tolerance."""
+    h, R, _ = gapped_router(E, d, dt, 7000 + d)
+    idx, gate = A.ada_pregate(h.to(DEV), R.to(DEV), k, renorm=renorm)
+    sync()
+    ridx, rg = O.pregate(to64(h), to64(R), k, renorm)
+    assert idx.cpu().numpy().tolist() == ridx.tolist(), (E, k, d)
+    check_close(gate, rg, GATE_RTOL, GATE_ATOL, "gates")
+
+
 def test_pregate_ties_go_to_the_lower_index():
     # identical router rows give identical logits (same summation order per row)
     E, d = 8, 512
