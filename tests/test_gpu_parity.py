@@ -748,6 +748,57 @@ def test_decode_gemv_layer_is_the_per_projection_gemv(dt):
         assert np.all(np.abs(to64(y) - ref) <= gemv_bound(W64, x64, ref, dt))
 
 
+def _random_layer_cases(n: int = 8, seed: int = 20261206):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        n_proj = int(rng.integers(1, 17))
+        shapes = [(8 * int(rng.integers(1, 200)), 8 * int(rng.integers(1, 200))) for _ in range(n_proj)]
+        out.append((c, "bf16" if rng.random() < 0.75 else "fp32", shapes))
+    return out
+
+
+@pytest.mark.parametrize("case,dt,shapes", _random_layer_cases())
+def test_gemv_layer_and_lora_paths_on_random_groups(case, dt, shapes):
+    """Seeded draws of 1 to 16 projections of ragged shapes in one group: the GEMV-layer
+    launch bit-identical to per-projection GEMVs and within the oracle's bound; the
+    fused unmerged layer path and the batched path (3 requests) within the bound of the
+    oracle's routed forward."""
+    E, r, k, nb = 6, 8, 2, 3
+    banks = [synth.adapter_bank(1300 + 37 * case + i, E, r, do, di, dt) for i, (do, di) in enumerate(shapes)]
+    xs = [synth.host_normal(synth.tensor_seed(1400 + 37 * case + i, di), (nb, di), 1.0, dt)
+          for i, (_, di) in enumerate(shapes)]
+    dev = [tuple(t.to(DEV) for t in b) for b in banks]
+    xd = [x.to(DEV) for x in xs]
+    sels = [make_selection(E, k, 64, dt, 80 + 7 * b) for b in range(nb)]
+    idx = torch.stack([s_[0] for s_ in sels]).contiguous()
+    gate = torch.stack([s_[1] for s_ in sels]).contiguous()
+    didx, dgate = idx.to(DEV), gate.to(DEV)
+    yl = [torch.full((do,), float("nan"), dtype=TD[dt], device=DEV) for do, _ in shapes]
+    A.ada_decode_gemv_layer([(w, x[0], y) for (w, _, _), x, y in zip(dev, xd, yl)])
+    one = [A.ada_decode_gemv(w, x[0]) for (w, _, _), x in zip(dev, xd)]
+    yf = [torch.full((do,), float("nan"), dtype=TD[dt], device=DEV) for do, _ in shapes]
+    A.ada_lora_layer([(w, a, b, x[0], y) for (w, a, b), x, y in zip(dev, xd, yf)], didx[0].contiguous(),
+                     dgate[0].contiguous(), 2.0)
+    yb = [torch.full((nb, do), float("nan"), dtype=TD[dt], device=DEV) for do, _ in shapes]
+    A.ada_lora_batch([(w, a, b, x, y) for (w, a, b), x, y in zip(dev, xd, yb)], didx, dgate, 2.0)
+    sync()
+    iv = torch.int16 if dt == "bf16" else torch.int32
+    for (W, Aw, Bw), x, y, y1, f, bt in zip(banks, xs, yl, one, yf, yb):
+        assert torch.equal(y.cpu().view(iv), y1.cpu().view(iv))
+        W64, A64, B64 = to64(W), to64(Aw), to64(Bw)
+        x64 = to64(x[0])
+        ref = O.gemv(W64, x64)
+        assert np.all(np.abs(to64(y) - ref) <= gemv_bound(W64, x64, ref, dt))
+        for b in range(nb):
+            xb = to64(x[b])
+            rb = O.routed_lora_forward(W64, A64, B64, idx[b].numpy(), gate[b].numpy().astype(np.float64), 2.0, xb)
+            lim = gemv_bound(W64, xb, rb, dt) + 1e-4 * (np.abs(W64) @ np.abs(xb))
+            assert np.all(np.abs(to64(bt[b]) - rb) <= lim), ("batch", b)
+            if b == 0:
+                assert np.all(np.abs(to64(f) - rb) <= lim), "layer"
+
+
 # ---------------------------------------------------------------- graph capture
 
 
