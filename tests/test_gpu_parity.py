@@ -69,6 +69,24 @@ def test_pregate_matches_oracle_on_random_shapes(E, k, d, dt, renorm):
     check_close(gate, rg, GATE_RTOL, GATE_ATOL, "gates")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_pregate_with_nan_scores_still_selects_distinct_in_range_experts(dt):
+    """A NaN in the hidden state makes every logit NaN, and NaN rows of the router make
+    some of them NaN: the selection is then unspecified, but it must still be k
+    distinct indices in [0, E), so a merge never reads outside the adapter banks."""
+    E, k, d = 16, 4, 256
+    h, R, _ = gapped_router(E, d, dt, 77)
+    h_nan = h.clone()
+    h_nan[3] = float("nan")
+    R_nan = R.clone()
+    R_nan[[2, 9]] = float("nan")
+    for hh, RR in ((h_nan, R), (h, R_nan)):
+        idx, _ = A.ada_pregate(hh.to(DEV), RR.to(DEV), k)
+        sync()
+        got = idx.cpu().tolist()
+        assert len(set(got)) == k and all(0 <= e < E for e in got), got
+
+
 def test_pregate_ties_go_to_the_lower_index():
     # identical router rows give identical logits (same summation order per row)
     E, d = 8, 512
