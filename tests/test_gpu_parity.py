@@ -817,6 +817,38 @@ def test_gemv_layer_and_lora_paths_on_random_groups(case, dt, shapes):
                 assert np.all(np.abs(to64(f) - rb) <= lim), "layer"
 
 
+def test_calls_run_in_order_on_the_callers_streams():
+    """Every call enqueues on the stream it is given (torch's current stream by
+    default): two models merged concurrently on two side streams, each followed on its
+    own stream by a copy of its result, match the oracle; a third call given an
+    explicit stream that waits on the others sees both merges."""
+    E, r, k = 8, 16, 2
+    banks = [synth.adapter_bank(1500 + i, E, r, 520, 264, "bf16") for i in range(2)]
+    idx, gate = make_selection(E, k, 64, "bf16", 21)
+    refs = [O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), gate.numpy().astype(np.float64), 2.0)
+            for W, Aw, Bw in banks]
+    ws = [W.to(DEV) for W, _, _ in banks]
+    models = [A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r) for w, (_, Aw, Bw) in zip(ws, banks)]
+    didx, dgate = idx.to(DEV), gate.to(DEV)
+    sync()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    copies = []
+    for m, w, st in zip(models, ws, streams):
+        with torch.cuda.stream(st):
+            A.ada_merge(m, didx, dgate, 2.0)
+            copies.append(w.clone())
+    joined = torch.cuda.Stream()
+    for st in streams:
+        joined.wait_stream(st)
+    A.ada_unmerge(models[0], didx, dgate, 2.0, stream=joined)
+    sync()
+    for c, ref in zip(copies, refs):
+        check_close(c, ref, *tol(torch.bfloat16), "merge on a side stream")
+    check_close(ws[0], to64(banks[0][0]), *tol(torch.bfloat16), "unmerge on an explicit stream")
+    for m in models:
+        m.destroy()
+
+
 # ---------------------------------------------------------------- graph capture
 
 
