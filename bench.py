@@ -241,7 +241,30 @@ def cpu_baseline(cfg, seed, target_s, max_layers=0):
                   f"{target_s:g} s of oracle time): pregate + merge + unmerge in fp64 NumPy, {sec:.2f} s; "
                   f"each layer's inputs copied to host before its timing",
         "seconds": round(sec, 3),
+        "host": host_description(),
     }
+
+
+def host_description() -> dict:
+    """The host the CPU baseline ran on: CPU model and the BLAS NumPy calls."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy as np
+
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "logical_cpus_visible": len(os.sched_getaffinity(0))}
 
 
 def time_ms(torch, fn, reps):
