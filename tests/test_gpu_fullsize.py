@@ -18,8 +18,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def run_stack(cfg, seed, full_check):
-    """full_check(l, p, proj) -> True for the projections compared element by element."""
+def run_stack(cfg, seed, full_check, decode_check=False):
+    """full_check(l, p, proj) -> True for the projections compared element by element.
+    decode_check: also decode every fully kept projection on the merged weights and
+    compare with the oracle's routed forward on the original ones (relative L2 <= 5e-3,
+    the merged-vs-routed criterion)."""
     h, R, seed = gapped_stack_router(cfg, seed)
     ridx, rg = O.pregate(to64(h), to64(R), cfg.k, cfg.renorm)
     st = synth.make_stack(cfg, seed, device=DEV)
@@ -44,6 +47,17 @@ def run_stack(cfg, seed, full_check):
         check_close(got, ref, BF16_RTOL, BF16_ATOL, f"merge layer {l} proj {cfg.projections[p].name}")
         n_checked += got.numel()
 
+    if decode_check:
+        for l, p, rows, w0 in keep:
+            if len(rows) != cfg.projections[p].d_out:
+                continue
+            x = synth.host_normal(synth.tensor_seed(seed, "x", l, p), (w0.shape[1],), 1.0, "bf16")
+            y = A.ada_decode_gemv(st.W[l][p], x.to(DEV))
+            torch.cuda.synchronize()
+            ref = O.routed_lora_forward(to64(w0), to64(st.A[l][p]), to64(st.B[l][p]), ridx, rg, cfg.scale, to64(x))
+            rel = np.linalg.norm(to64(y) - ref) / np.linalg.norm(ref)
+            assert rel <= 5e-3, (l, cfg.projections[p].name, rel)
+
     A.ada_unmerge(model, idx, gate, cfg.scale)
     torch.cuda.synchronize()
     exact = total = 0
@@ -60,7 +74,7 @@ def run_stack(cfg, seed, full_check):
 
 
 def test_llama7b_e8r16k2_stack():
-    frac = run_stack(LLAMA7B_E8R16K2, 1000, lambda l, p, proj: l == 0)
+    frac = run_stack(LLAMA7B_E8R16K2, 1000, lambda l, p, proj: l == 0, decode_check=True)
     assert frac > 0.8
 
 
