@@ -3,14 +3,17 @@
 
 One step = ada_pregate (router GEMV + top-k + gates) -> ada_merge (every layer and
 projection, in place, one launch) -> ada_unmerge (one launch), on a seeded synthetic
-stack already resident in HBM.  The default workload is the Llama-2-7B-shaped stack
-with E=8 adapters of rank 16 per projection and top-2 gating (bf16).
+stack already resident in HBM.  The default workload is the largest that fits one
+GPU: the Llama-2-70B-shaped stack (137 GB of bf16 weights, 560 projections) with E=8
+adapters of rank 16 per projection and top-2 gating, merged in place.
 
 Prints one JSON line.  `value` is the whole step's algorithmic HBM bytes (W read and
 written by merge and by unmerge, the selected adapters read by each, the router read
 by pregate) divided by the measured step time.  `roofline` reports the merge kernel
 alone: algorithmic bytes per launch over its mean duration from HIP events recorded
-on the launch stream inside the timed region.
+on the launch stream inside the timed region.  After the headline stack is freed,
+the 7B-shaped stacks (rank 16 top-2, and rank 64 top-4) are timed the same way and
+reported under `other_workloads`.
 """
 from __future__ import annotations
 
@@ -28,7 +31,12 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 VALU_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector peak
 METRIC = "full-model adapter merge: effective HBM GB/s (% of peak) and merge µs"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "merge_bf16_traffic.txt")
+DEFAULT_WORKLOAD = "llama70b_e8r16k2"
+DEFAULT_EXTRA = "llama7b_e8r16k2,llama7b_e16r64k4"
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"merge_bf16_traffic_{workload}.txt")
 
 
 def parse():
@@ -36,9 +44,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b_e8r16k2",
-                    help="preset: llama7b_e8r16k2 (default), llama7b_e16r64k4, llama70b_e8r16k2, "
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="preset: llama70b_e8r16k2 (default), llama7b_e8r16k2, llama7b_e16r64k4, "
                          "llama70b_tp8_e8r16k2, e2e_llama7b, tiny")
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
+                    help="comma-separated presets timed after the headline (merge only, in place); '' for none")
     ap.add_argument("--out-of-place", action="store_true", help="merge into a separate W' buffer")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
@@ -49,10 +59,15 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
-                    help="write profiles/merge_bf16_traffic.txt from four rocprofv3 --pmc output folders "
+                    help="write profiles/merge_bf16_traffic_<workload>.txt from four rocprofv3 --pmc output folders "
                          "(FETCH_SIZE and WRITE_SIZE of this workload's bench run, then of --calibrate-copy "
                          "--calibrate-mib MiB) and exit; needs no GPU")
     ap.add_argument("--calibrate-mib", type=int, default=1024)
+    ap.add_argument("--trace-summary", nargs=2, metavar=("DIR", "OUT"),
+                    help="write a markdown summary (OUT, under profiles/) of a rocprofv3 --kernel-trace run of this "
+                         "command line's workload found under DIR, the timed launches averaged apart from the "
+                         "warm-up ones, and exit; needs no GPU")
+    ap.add_argument("--trace-command", default="", help="the profiled command, quoted in the trace summary")
     return ap.parse_args()
 
 
@@ -79,7 +94,7 @@ def kernel_sha() -> str:
 def read_traffic(workload: str, mode: str, path=None):
     """HBM bytes per merge launch from the committed rocprofv3 counter summary, or
     None when the summary is missing or was taken on a different kernel source."""
-    path = path or TRAFFIC_FILE
+    path = path or traffic_file(workload)
     if not os.path.exists(path):
         return None
     rec = {}
@@ -117,7 +132,7 @@ def counter_mean(folder: str, counter: str, kernel_substr: str):
 def write_traffic(args, cfg, out=None):
     """HBM bytes of one merge launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for torch.neg over a known size."""
-    out = out or TRAFFIC_FILE
+    out = out or traffic_file(cfg.name)
     fdir, wdir, cfdir, cwdir = args.traffic_from
     f, nf, names = counter_mean(fdir, "FETCH_SIZE", "merge_bf16_kernel")
     w, nw, _ = counter_mean(wdir, "WRITE_SIZE", "merge_bf16_kernel")
@@ -128,7 +143,7 @@ def write_traffic(args, cfg, out=None):
     rd, wr = f * 1024 * rf, w * 1024 * wf
     alg = cfg.merge_bytes()
     mode = "out_of_place" if args.out_of_place else "in_place"
-    flags = (" --workload " + cfg.name if cfg.name != "llama7b_e8r16k2" else "") + \
+    flags = (" --workload " + cfg.name if cfg.name != DEFAULT_WORKLOAD else "") + \
         (" --out-of-place" if args.out_of_place else "")
     kname = names[0].replace("void ada::(anonymous namespace)::", "").split("(")[0]
     lines = [
@@ -137,9 +152,9 @@ def write_traffic(args, cfg, out=None):
         "# Commands (each a pass of its own, run from the repository root on one MI355X):",
         "#   export TMPDIR=/tmp",
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fdir} -o f -- python3 bench.py --steps 2 "
-        f"--warmup 1 --no-cpu-baseline --no-copy-ceiling{flags}",
+        f"--warmup 1 --no-cpu-baseline --no-copy-ceiling --extra ''{flags}",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wdir} -o w -- python3 bench.py --steps 2 "
-        f"--warmup 1 --no-cpu-baseline --no-copy-ceiling{flags}",
+        f"--warmup 1 --no-cpu-baseline --no-copy-ceiling --extra ''{flags}",
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfdir} -o f -- python3 bench.py "
         f"--calibrate-copy {args.calibrate_mib}",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwdir} -o w -- python3 bench.py "
@@ -219,10 +234,13 @@ def cpu_baseline(cfg, seed, target_s, max_layers=0):
     idx, g = O.pregate(h64, R64, cfg.k, cfg.renorm)
     sec = time.perf_counter() - t0
     done = 0
+    copy_s = 0.0
     while done < limit and (done == 0 or sec < target_s):
         W, A, B = synth.draw_layer(cfg, seed, done, device="cuda")  # layer `done` of the GPU stack
+        t0 = time.perf_counter()
         host = [(w.double().cpu().numpy(), a.double().cpu().numpy(), b.double().cpu().numpy())
                 for w, a, b in zip(W, A, B)]
+        copy_s += time.perf_counter() - t0
         del W, A, B
         t0 = time.perf_counter()
         for Wh, Ah, Bh in host:
@@ -241,6 +259,7 @@ def cpu_baseline(cfg, seed, target_s, max_layers=0):
                   f"{target_s:g} s of oracle time): pregate + merge + unmerge in fp64 NumPy, {sec:.2f} s; "
                   f"each layer's inputs copied to host before its timing",
         "seconds": round(sec, 3),
+        "device_to_host_copy_seconds": round(copy_s, 3),
         "host": host_description(),
     }
 
@@ -399,8 +418,7 @@ def run_e2e(args, cfg, torch, A, synth, dev):
     merged_pp_graph = time_ms(torch, g_merged_pp.replay, reps)
     del g_merged_pp
     A.ada_unmerge(model, idx, gate, cfg.scale)
-    # N1: fused switch between two selections (undo prev + apply cur in one pass), and
-    # N2: switching every decode token (each token pays a full switch)
+    # N1: fused in-place switch between two selections (undo prev + apply cur in one pass)
     h2, R2 = synth.router_inputs(cfg, args.seed + 1)
     h2 = h2.to(dev)
     idx2 = torch.empty(cfg.k, dtype=torch.int32, device=dev)
@@ -416,10 +434,47 @@ def run_e2e(args, cfg, torch, A, synth, dev):
         flip[0] = 1 - flip[0]
 
     t_switch = time_ms(torch, switch_once, 6)
-    per_token_switch = time_ms(torch, lambda: (switch_once(), token_merged()), reps)
     if flip[0]:
         switch_once()
     A.ada_unmerge(model, idx, gate, cfg.scale)
+    torch.cuda.synchronize()
+    # N2: a new selection every decode token, served drift-free: each token is pre-gated
+    # on its own hidden state and re-merged from the untouched W into W' (an out-of-place
+    # model: one read of W and one write of W' per token, like a switch, and no rounding
+    # carried from token to token), then decoded on W'
+    wout = [[torch.empty_like(st.W[l][p]) for p in range(len(cfg.projections))] for l in range(cfg.n_layers)]
+    model_oop = A.AdaModel([(st.W[l][p], wout[l][p], st.A[l][p], st.B[l][p]) for l, p, _ in st.items()],
+                           cfg.E, cfg.r)
+    hs = [h, h2]
+    tok = [0]
+
+    def token_on_wout():
+        for l in range(cfg.n_layers):
+            for grp in groups:
+                A.ada_decode_gemv_layer([(wout[l][p], x[names[p]], ys[l][p]) for p in grp])
+
+    def token_remerge(ht):
+        A.ada_pregate(ht, R, cfg.k, cfg.renorm, idx, gate)
+        A.ada_merge(model_oop, idx, gate, cfg.scale)
+        token_on_wout()
+
+    def token_remerge_eager():
+        token_remerge(hs[tok[0]])
+        tok[0] ^= 1
+
+    t_remerge = time_ms(torch, lambda: (A.ada_pregate(h2, R, cfg.k, cfg.renorm, idx, gate),
+                                        A.ada_merge(model_oop, idx, gate, cfg.scale)), 6)
+    per_token_remerge_eager = time_ms(torch, token_remerge_eager, reps)
+    g_re = [graph_of(lambda hh=hh: token_remerge(hh)) for hh in hs]
+    rep_i = [0]
+
+    def replay_remerge():
+        g_re[rep_i[0]].replay()
+        rep_i[0] ^= 1
+
+    per_token_remerge_graph = time_ms(torch, replay_remerge, reps)
+    del g_re, model_oop, wout
+    torch.cuda.empty_cache()
     base_eager = time_ms(torch, token_baseline, max(2, reps // 4))
     g_base = graph_of(token_baseline)
     base_graph = time_ms(torch, g_base.replay, reps)
@@ -463,7 +518,7 @@ def run_e2e(args, cfg, torch, A, synth, dev):
             "vs_batch1_merged_tokens_per_s": round(nb * merged_graph / t_batch, 3),
             # derived, not timed: serving the same requests one at a time on merged
             # weights, switching the selection before each request's token
-            "serial_switching_step_ms_derived": round(nb * (t_switch + merged_graph), 3),
+            "serial_switching_step_ms_derived": round(nb * (t_remerge + merged_graph), 3),
         }
         del yb, bws, xb
 
@@ -504,9 +559,11 @@ def run_e2e(args, cfg, torch, A, synth, dev):
             "request_adafuse_eager": round(req_eager, 3),
             "request_baseline_eager": round(req_base_eager, 3),
             "simple_fusion_merge": round(simple, 3),
-            "switch": round(t_switch, 3),
-            "token_with_switch_eager": round(per_token_switch, 4),
-            "request_switch_every_token_eager": round(steps * per_token_switch + t_pregate, 3),
+            "switch_in_place": round(t_switch, 3),
+            "pregate_plus_remerge": round(t_remerge, 3),
+            "token_with_remerge_eager": round(per_token_remerge_eager, 4),
+            "token_with_remerge_graph": round(per_token_remerge_graph, 4),
+            "request_remerge_every_token_graph": round(steps * per_token_remerge_graph, 3),
         },
         "decode_GBps_merged_graph": round(token_bytes / (merged_graph * 1e-3) / 1e9, 1),
         "launches_per_token": {"merged": launches_merged, "merged_per_projection": cfg.n_layers * len(names),
@@ -523,12 +580,151 @@ def run_e2e(args, cfg, torch, A, synth, dev):
     print(json.dumps(out), flush=True)
 
 
+def kernel_short_name(name: str) -> str:
+    return name.replace("void ada::(anonymous namespace)::", "ada::").split("(")[0]
+
+
+def trace_summary(args, cfg):
+    """Markdown summary of a rocprofv3 --kernel-trace run of this workload (default
+    flags otherwise): every kernel's calls and mean duration, and the merge kernel's
+    launches split into warm-up and timed ones (merge and unmerge alternate, the timed
+    ones are the last 2 x steps), with the timed mean's algorithmic GB/s."""
+    import csv
+    import glob
+
+    folder, out = args.trace_summary
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                rows.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]), row["Kernel_Name"]))
+    if not rows:
+        raise SystemExit(f"no kernel_trace.csv under {folder}")
+    rows.sort()
+    agent = "gfx950"
+    stats = {}
+    for t0, t1, name in rows:
+        k = kernel_short_name(name)
+        c, tot = stats.get(k, (0, 0.0))
+        stats[k] = (c + 1, tot + (t1 - t0) / 1e3)
+    grand = sum(t for _, t in stats.values())
+    merge = [(t0, t1, kernel_short_name(n)) for t0, t1, n in rows if "merge_bf16_kernel" in n or "merge_f32_kernel" in n]
+    n_timed = 2 * args.steps
+    if len(merge) != 2 * (args.steps + args.warmup):
+        raise SystemExit(f"expected {2 * (args.steps + args.warmup)} merge launches, found {len(merge)}: pass the "
+                         "profiled run's --steps/--warmup")
+    timed = [(t1 - t0) / 1e3 for t0, t1, _ in merge[-n_timed:]]
+    warm = [(t1 - t0) / 1e3 for t0, t1, _ in merge[:-n_timed]]
+    mean_t = sum(timed) / len(timed)
+    alg = cfg.merge_bytes()
+    lines = [
+        f"# rocprofv3 kernel trace: merge on `{cfg.name}` ({cfg.note})",
+        "",
+        "Command (from the repository root on one MI355X), and the summary's own command:",
+        "",
+        "```",
+        f"export TMPDIR=/tmp; {args.trace_command}",
+        f"python3 bench.py --workload {cfg.name} --steps {args.steps} --warmup {args.warmup} "
+        f"--trace-summary {folder} {out}",
+        "```",
+        "",
+        f"Agent: {agent}",
+        "",
+        "| kernel | calls | total µs | avg µs | % |",
+        "|---|---|---|---|---|",
+    ]
+    for k, (c, tot) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| `{k[:90]}` | {c} | {tot:.1f} | {tot / c:.2f} | {100 * tot / grand:.1f} |")
+    lines += [
+        "",
+        f"Merge kernel code hash (bench.py kernel_sha, comments aside): {kernel_sha()}.",
+        f"Merge kernel launches: {len(merge)} = {args.warmup} warm-up and {args.steps} timed steps, one merge and "
+        f"one unmerge each (`{merge[-1][2]}`).",
+        f"- warm-up launches: mean {sum(warm) / max(1, len(warm)):.1f} µs over {len(warm)}",
+        f"- timed launches: mean {mean_t:.1f} µs, min {min(timed):.1f}, max {max(timed):.1f} over {len(timed)}",
+        f"- algorithmic bytes per launch {alg:,} -> {alg / mean_t / 1e3:.0f} GB/s over the timed mean, "
+        f"{alg / mean_t / 1e3 / HBM_PEAK_GBPS * 100:.1f}% of {HBM_PEAK_GBPS:.0f} GB/s",
+        f"- two timed launches per step: {2 * mean_t / 1e3:.3f} ms of kernel time per step",
+    ]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}: timed merge mean {mean_t:.1f} µs ({alg / mean_t / 1e3:.0f} GB/s)")
+
+
+def time_merge_workload(cfg, args, torch, A, synth, dev, steps, warmup, out_of_place):
+    """Generate the stack in HBM, then warm-up and timed steps of pregate + merge +
+    unmerge; returns the timings (HIP events on the launch stream) and the footprint.
+    Frees the stack before returning."""
+    torch.cuda.reset_peak_memory_stats(dev)
+    t_gen = time.perf_counter()
+    st = synth.make_stack(cfg, args.seed, device=dev)
+    h, R = synth.router_inputs(cfg, args.seed)
+    h, R = h.to(dev), R.to(dev)
+    projs = []
+    for l, p, _ in st.items():
+        w = st.W[l][p]
+        projs.append((w, torch.empty_like(w) if out_of_place else None, st.A[l][p], st.B[l][p]))
+    model = A.AdaModel(projs, cfg.E, cfg.r)
+    idx = torch.empty(cfg.k, dtype=torch.int32, device=dev)
+    gate = torch.empty(cfg.k, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        A.ada_pregate(h, R, cfg.k, cfg.renorm, idx, gate)
+        if evs:
+            evs[1].record()
+        A.ada_merge(model, idx, gate, cfg.scale)
+        if evs:
+            evs[2].record()
+        A.ada_unmerge(model, idx, gate, cfg.scale)
+        if evs:
+            evs[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# workload {cfg.name}: {cfg.weight_elems() / 1e9:.2f}G weights, {model.tiles} tiles, "
+          f"generated in {gen_s:.1f}s; timing {steps} steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {
+        "wall": wall,
+        "pre_ms": [e[0].elapsed_time(e[1]) for e in evs],
+        "merge_ms": [e[1].elapsed_time(e[2]) for e in evs],
+        "unmerge_ms": [e[2].elapsed_time(e[3]) for e in evs],
+        "tiles": model.tiles,
+        "table_bytes": model.device_bytes,
+        "peak_torch_bytes": torch.cuda.max_memory_allocated(dev),
+    }
+    del model, projs, st, h, R, idx, gate
+    torch.cuda.empty_cache()
+    return res
+
+
+def merge_summary(cfg, res, mode):
+    merge_ms = res["merge_ms"]
+    mean_s = sum(merge_ms) / len(merge_ms) / 1e3
+    achieved = cfg.merge_bytes() / mean_s / 1e9
+    traffic = read_traffic(cfg.name, mode)
+    return mean_s, achieved, traffic
+
+
 def main():
     args = parse()
-    if args.traffic_from:
-        from weight_merge_amd.configs import PRESETS
+    from weight_merge_amd.configs import PRESETS
 
+    if args.traffic_from:
         return write_traffic(args, PRESETS[args.workload])
+    if args.trace_summary:
+        return trace_summary(args, PRESETS[args.workload])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the merge needs no communication between GPUs (each merges "
@@ -539,7 +735,6 @@ def main():
 
     from weight_merge_amd import api as A
     from weight_merge_amd import synth
-    from weight_merge_amd.configs import PRESETS
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -561,67 +756,41 @@ def main():
     if cfg.decode_steps:
         return run_e2e(args, cfg, torch, A, synth, dev)
     mode = "out_of_place" if args.out_of_place else "in_place"
-    t_gen = time.perf_counter()
-    st = synth.make_stack(cfg, args.seed, device=dev)
-    h, R = synth.router_inputs(cfg, args.seed)
-    h, R = h.to(dev), R.to(dev)
-    projs = []
-    for l, p, _ in st.items():
-        w = st.W[l][p]
-        projs.append((w, torch.empty_like(w) if args.out_of_place else None, st.A[l][p], st.B[l][p]))
-    model = A.AdaModel(projs, cfg.E, cfg.r)
-    idx = torch.empty(cfg.k, dtype=torch.int32, device=dev)
-    gate = torch.empty(cfg.k, dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    gen_s = time.perf_counter() - t_gen
+    res = time_merge_workload(cfg, args, torch, A, synth, dev, args.steps, args.warmup, args.out_of_place)
 
-    def step(evs=None):
-        if evs:
-            evs[0].record()
-        A.ada_pregate(h, R, cfg.k, cfg.renorm, idx, gate)
-        if evs:
-            evs[1].record()
-        A.ada_merge(model, idx, gate, cfg.scale)
-        if evs:
-            evs[2].record()
-        A.ada_unmerge(model, idx, gate, cfg.scale)
-        if evs:
-            evs[3].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"# workload {cfg.name}: {cfg.weight_elems() / 1e9:.2f}G weights, {model.tiles} tiles, "
-          f"generated in {gen_s:.1f}s; timing {args.steps} steps", file=sys.stderr, flush=True)
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    unmerge_ms = [e[2].elapsed_time(e[3]) for e in evs]
     merge_bytes = cfg.merge_bytes()
     pregate_bytes = (cfg.E * cfg.d_model + cfg.d_model) * cfg.elem_bytes
     step_bytes = 2 * merge_bytes + pregate_bytes
-    ms_per_step = wall * 1e3 / args.steps
-    value = step_bytes * args.steps / wall / 1e9
-    merge_mean_s = sum(merge_ms) / len(merge_ms) / 1e3
-    achieved = merge_bytes / merge_mean_s / 1e9
-    traffic = read_traffic(cfg.name, mode)
-    n_tiles = model.tiles
+    ms_per_step = res["wall"] * 1e3 / args.steps
+    value = step_bytes * args.steps / res["wall"] / 1e9
+    merge_mean_s, achieved, traffic = merge_summary(cfg, res, mode)
+    merge_ms, unmerge_ms, pre_ms = res["merge_ms"], res["unmerge_ms"], res["pre_ms"]
 
     torch_copy = None if args.no_copy_ceiling else torch_copy_rate(torch, dev)
-
-    del model, projs, st
-    torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.seed, args.cpu_sample_seconds,
                                                           args.cpu_sample_layers)
 
+    others = {}
+    for name in [n for n in args.extra.split(",") if n]:
+        ocfg = PRESETS[name]
+        ores = time_merge_workload(ocfg, args, torch, A, synth, dev, args.steps, args.warmup, False)
+        o_mean_s, o_ach, o_traffic = merge_summary(ocfg, ores, "in_place")
+        others[name] = {
+            "workload": ocfg.note,
+            "mode": "in_place",
+            "merge_us_mean": round(o_mean_s * 1e6, 1),
+            "merge_us_median": round(pct(ores["merge_ms"], 0.5) * 1e3, 1),
+            "unmerge_us_median": round(pct(ores["unmerge_ms"], 0.5) * 1e3, 1),
+            "merge_algorithmic_bytes": ocfg.merge_bytes(),
+            "achieved_GBps": round(o_ach, 2),
+            "frac": round(o_ach / HBM_PEAK_GBPS, 4),
+            "traffic": None if o_traffic is None else int(o_traffic),
+            "target_us_at_70pct": round(ocfg.merge_bytes() / (0.7 * HBM_PEAK_GBPS * 1e3), 1),
+            "contraction_frac_of_mfma_peak": round(ocfg.merge_flops() / o_mean_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        }
+
+    wbytes = cfg.weight_elems() * cfg.elem_bytes
+    abytes = cfg.adapter_bank_bytes()
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -642,8 +811,8 @@ def main():
             "E": cfg.E, "r": cfg.r, "k": cfg.k, "scale": cfg.scale,
             "mode": mode,
             "step": "pregate + merge + unmerge",
-            "weights_GB": round(cfg.weight_elems() * cfg.elem_bytes / 1e9, 3),
-            "merge_tiles": n_tiles,
+            "weights_GB": round(wbytes / 1e9, 3),
+            "merge_tiles": res["tiles"],
         },
         "merge_us": {"mean": round(merge_mean_s * 1e6, 1), "median": round(pct(merge_ms, 0.5) * 1e3, 1),
                      "min": round(min(merge_ms) * 1e3, 1), "p90": round(pct(merge_ms, 0.9) * 1e3, 1)},
@@ -674,7 +843,18 @@ def main():
             "frac": round(cfg.merge_flops() / merge_mean_s / 1e12
                           / (MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else VALU_F32_PEAK_TFLOPS), 4),
         },
+        # device footprint beside the base weights: every adapter bank (all E experts of
+        # every projection), the merge's work tables, the router and selection
+        "memory": {
+            "weights_bytes": wbytes,
+            "adapter_banks_bytes": abytes,
+            "work_table_bytes": res["table_bytes"],
+            "peak_device_bytes": res["peak_torch_bytes"] + res["table_bytes"],
+            "peak_over_weights": round((res["peak_torch_bytes"] + res["table_bytes"]) / wbytes - 1, 4),
+            "out_of_place_copy_bytes": wbytes if args.out_of_place else 0,
+        },
         "cpu_baseline": cpu,
+        "other_workloads": others,
     }
     print(json.dumps(out), flush=True)
 

@@ -72,26 +72,36 @@ typedef struct ada_model_s* ada_model;
  * Register a stack of adapted projections (every layer and projection of a
  * model, in any order).  Builds the per-projection work table the one-launch
  * merge walks ([ja] 2.2: the large product is split into GEMM tiles assigned to
- * thread blocks) and copies it to the current device; this is the only call that
- * allocates (one table per contraction class, three in all: ~64 bytes per projection
- * each plus a small tile index).
+ * thread blocks) and uploads it to the current device; this is the only call that
+ * allocates (one device allocation for one table per contraction class, three in
+ * all: ~64 bytes per projection each plus a small tile index, and the tables' host
+ * image, kept until destroy).
  * n_proj >= 1; all projections share E, r and dtype.  On success *out owns the
  * table until ada_model_destroy.  ada_merge, ada_unmerge and ada_switch return
  * ADA_EINVAL when another device is current than at creation.  The registered pointers must stay valid, and
  * may not be registered twice in one model.  An out-of-place w_out must not overlap
  * any registered w, w_out, a or b (the launch reads and writes all tiles at once).
+ * Ordering: the table is copied to the device asynchronously on `stream` (a
+ * hipStream_t as void*, NULL = the default stream).  Merges enqueued on that stream
+ * after this call see it; a merge on another stream must be ordered after `stream`
+ * by the caller (for instance by synchronizing `stream` once).  Argument checks run
+ * before any HIP call; on an error nothing is allocated and *out is NULL.
  */
 int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r,
-                     int32_t dtype, ada_model* out);
+                     int32_t dtype, void* stream, ada_model* out);
 
-/* Free the model's work table.  NULL is ignored.  Call after the model's last
- * enqueued merge has completed. */
+/* Free the model's work table (waiting first for its upload).  NULL is ignored.
+ * Call after the model's last enqueued merge has completed. */
 void ada_model_destroy(ada_model m);
 
 /* Number of output tiles one merge launch of this model covers at k*r <= 32
  * (32 x 256 tiles for bf16, 64 x 64 for fp32; for measurement); negative status on
  * a bad handle. */
 int64_t ada_model_tiles(ada_model m);
+
+/* Device bytes the model owns (its work tables), for footprint reports; negative
+ * status on a bad handle. */
+int64_t ada_model_device_bytes(ada_model m);
 
 /*
  * Token-level pre-gating ([pt] 2.A; [ja] 2.1).  z = R h (fp32 accumulation);

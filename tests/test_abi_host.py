@@ -83,15 +83,15 @@ def proj(**kw):
 def create(lib, projs, E=4, r=8, dt=ADA_F32):
     arr = (AdaProj * len(projs))(*projs)
     h = ctypes.c_void_p()
-    st = lib.ada_model_create(arr, len(projs), E, r, dt, ctypes.byref(h))
+    st = lib.ada_model_create(arr, len(projs), E, r, dt, None, ctypes.byref(h))
     assert h.value is None  # nothing allocated on failure
     return st
 
 
 def test_model_create_validation(lib):
-    assert lib.ada_model_create(None, 1, 4, 8, ADA_F32, None) == ADA_EINVAL
+    assert lib.ada_model_create(None, 1, 4, 8, ADA_F32, None, None) == ADA_EINVAL
     arr = (AdaProj * 1)(proj())
-    assert lib.ada_model_create(arr, 1, 4, 8, ADA_F32, None) == ADA_EINVAL
+    assert lib.ada_model_create(arr, 1, 4, 8, ADA_F32, None, None) == ADA_EINVAL
     assert create(lib, [proj()], dt=5) == ADA_EDTYPE
     assert create(lib, [proj()], E=0) == ADA_ESHAPE
     assert create(lib, [proj()], E=65) == ADA_ESHAPE
@@ -110,7 +110,7 @@ def test_model_create_validation(lib):
     assert create(lib, [proj(), proj(d_out=1 << 23)]) == ADA_ESHAPE
     arr0 = (AdaProj * 1)(proj())
     h = ctypes.c_void_p()
-    assert lib.ada_model_create(arr0, 0, 4, 8, ADA_F32, ctypes.byref(h)) == ADA_ESHAPE
+    assert lib.ada_model_create(arr0, 0, 4, 8, ADA_F32, None, ctypes.byref(h)) == ADA_ESHAPE
 
 
 def test_merge_calls_reject_bad_handles(lib):

@@ -60,3 +60,33 @@ def test_kernel_identity_ignores_comments():
     code = "int f(int x) {\n  return x + 1;  // add one\n}\n"
     assert bench._code_only(code) == bench._code_only("/* doc\n   more */\n" + code.replace("// add one", "// +1"))
     assert bench._code_only(code) != bench._code_only(code.replace("+ 1", "+ 2"))
+
+
+def test_trace_summary_separates_timed_from_warm_up_launches(tmp_path):
+    """A synthetic rocprofv3 kernel trace of 1 warm-up and 2 timed steps: the summary
+    averages the last 2 x steps merge launches (merge and unmerge alternate) apart from
+    the warm-up ones."""
+    merge = "void ada::(anonymous namespace)::merge_bf16_kernel<32, 1, 8, 2, 0, false, 1>(ada::MergeParams)"
+    pre = "void ada::(anonymous namespace)::pregate_kernel<unsigned short>(...)"
+    folder = tmp_path / "trace"
+    folder.mkdir()
+    rows, t = [], 0
+    for dur in (9000, 9000, 4000, 4200, 4400, 4600):  # ns: warm-up merge+unmerge, then two timed steps
+        rows.append({"Kernel_Name": pre, "Start_Timestamp": t, "End_Timestamp": t + 5000})
+        t += 10000
+        rows.append({"Kernel_Name": merge, "Start_Timestamp": t, "End_Timestamp": t + dur})
+        t += dur + 100
+    with open(folder / "x_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+    out = str(tmp_path / "summary.md")
+    args = argparse.Namespace(trace_summary=[str(folder), out], steps=2, warmup=1, trace_command="rocprofv3 ...")
+    bench.trace_summary(args, PRESETS["llama7b_e8r16k2"])
+    text = open(out).read()
+    assert "timed launches: mean 4.3 µs" in text
+    assert "warm-up launches: mean 9.0 µs over 2" in text
+    args.warmup = 2  # a count that does not match the trace is refused
+    with pytest.raises(SystemExit):
+        bench.trace_summary(args, PRESETS["llama7b_e8r16k2"])

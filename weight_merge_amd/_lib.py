@@ -54,9 +54,10 @@ class AdaGemvProj(ctypes.Structure):
 _SIGNATURES = {
     "ada_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ada_model_create": (ctypes.c_int, [ctypes.POINTER(AdaProj), c_int32, c_int32, c_int32, c_int32,
-                                        ctypes.POINTER(c_void_p)]),
+                                        c_void_p, ctypes.POINTER(c_void_p)]),
     "ada_model_destroy": (None, [c_void_p]),
     "ada_model_tiles": (c_int64, [c_void_p]),
+    "ada_model_device_bytes": (c_int64, [c_void_p]),
     "ada_pregate": (ctypes.c_int, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                    c_void_p, c_void_p, c_void_p]),
     "ada_merge": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p]),

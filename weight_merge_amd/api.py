@@ -89,10 +89,12 @@ class AdaModel:
 
     projs: iterable of (w, w_out, a, b) with w [d_out, d_in] (row stride w.stride(0)),
     w_out None (merge in place) or a tensor like w, a [E, r, d_in], b [E, d_out, r].
-    The tensors must outlive the model; the model keeps references to them.
+    The tensors must outlive the model; the model keeps references to them.  The
+    work table is uploaded on `stream` (default: torch's current stream), which
+    orders it before the merges enqueued there.
     """
 
-    def __init__(self, projs, E: int, r: int):
+    def __init__(self, projs, E: int, r: int, stream=None):
         projs = list(projs)
         if not projs:
             raise ValueError("no projections")
@@ -115,7 +117,7 @@ class AdaModel:
                              _dev(a, "a"), _dev(b, "b"), d_out, d_in, w.stride(0))
             keep.append((w, w_out, a, b))
         handle = ctypes.c_void_p()
-        st = _lib.load().ada_model_create(arr, len(projs), E, r, _DT[dt], ctypes.byref(handle))
+        st = _lib.load().ada_model_create(arr, len(projs), E, r, _DT[dt], _stream(stream), ctypes.byref(handle))
         _check(st, "ada_model_create")
         self._h = handle
         self._keep = keep
@@ -131,6 +133,11 @@ class AdaModel:
     @property
     def tiles(self) -> int:
         return int(_lib.load().ada_model_tiles(self.handle))
+
+    @property
+    def device_bytes(self) -> int:
+        """Device memory the model owns (its work tables)."""
+        return int(_lib.load().ada_model_device_bytes(self.handle))
 
     def destroy(self):
         if getattr(self, "_h", None) is not None:

@@ -81,6 +81,10 @@ class StackConfig:
     def merge_flops(self) -> int:
         return 2 * self.k * self.r * self.weight_elems()
 
+    def adapter_bank_bytes(self) -> int:
+        """Every projection's whole bank of E adapters (A and B), resident beside W."""
+        return self.n_layers * sum(self.E * self.r * (p.d_in + p.d_out) for p in self.projections) * self.elem_bytes
+
     def decode_bytes_per_token(self) -> int:
         return self.weight_elems() * self.elem_bytes
 

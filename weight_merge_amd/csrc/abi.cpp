@@ -47,7 +47,9 @@ struct ada_model_s {
   int32_t r;
   int32_t n_proj;
   int32_t device;
-  void* dev;          // one allocation holding both tables
+  void* dev;          // one allocation holding every table
+  std::vector<unsigned char> host;  // the tables' host image, the source of the asynchronous upload
+  hipEvent_t uploaded;              // recorded on the creation stream after the upload
   TileTable tab[ada::kTileClasses];  // bf16: one per contraction class (32 x 256, 64 x 128, 128 x 128); fp32: all 64 x 64
 };
 
@@ -156,7 +158,7 @@ const char* ada_status_string(int status) {
 }
 
 int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r, int32_t dtype,
-                     ada_model* out) {
+                     void* stream, ada_model* out) {
   if (out == nullptr || projs == nullptr) return ADA_EINVAL;
   *out = nullptr;
   if (!dtype_ok(dtype)) return ADA_EDTYPE;
@@ -200,16 +202,29 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
   }
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return ADA_EHIP;
+  ada_model_s* m = new (std::nothrow) ada_model_s{};
+  if (m == nullptr) return ADA_ENOMEM;
+  m->host = std::move(host);
   void* dev = nullptr;
-  if (hipMalloc(&dev, bytes) != hipSuccess) return ADA_ENOMEM;
-  if (hipMemcpy(dev, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+  if (hipMalloc(&dev, bytes) != hipSuccess) {
+    delete m;
+    return ADA_ENOMEM;
+  }
+  // the upload is ordered on the caller's stream; the host image it reads lives in the
+  // model until destroy, which first waits for this event
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipEventCreateWithFlags(&m->uploaded, hipEventDisableTiming) != hipSuccess) {
     (void)hipFree(dev);
+    delete m;
     return ADA_EHIP;
   }
-  ada_model_s* m = new (std::nothrow) ada_model_s{};
-  if (m == nullptr) {
+  if (hipMemcpyAsync(dev, m->host.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipEventRecord(m->uploaded, s) != hipSuccess) {
+    (void)hipStreamSynchronize(s);
+    (void)hipEventDestroy(m->uploaded);
     (void)hipFree(dev);
-    return ADA_ENOMEM;
+    delete m;
+    return ADA_EHIP;
   }
   m->magic = kModelMagic;
   m->dtype = dtype;
@@ -233,6 +248,8 @@ int ada_model_create(const ada_proj* projs, int32_t n_proj, int32_t E, int32_t r
 void ada_model_destroy(ada_model m) {
   if (!model_ok(m)) return;
   m->magic = 0;
+  (void)hipEventSynchronize(m->uploaded);  // the upload reads m->host
+  (void)hipEventDestroy(m->uploaded);
   (void)hipFree(m->dev);
   delete m;
 }
@@ -240,6 +257,11 @@ void ada_model_destroy(ada_model m) {
 int64_t ada_model_tiles(ada_model m) {
   if (!model_ok(m)) return ADA_EINVAL;
   return m->tab[0].total_tiles;
+}
+
+int64_t ada_model_device_bytes(ada_model m) {
+  if (!model_ok(m)) return ADA_EINVAL;
+  return static_cast<int64_t>(m->host.size());
 }
 
 int ada_pregate(const void* h, const void* router, int32_t d, int32_t E, int32_t k, int32_t dtype,

@@ -94,6 +94,15 @@ __device__ __forceinline__ float row_dot(const T* __restrict__ rowp, const T* __
 
 constexpr int kGemvBatch = 8;
 
+// Order the LDS accesses of one wave: every write before the fence is complete and
+// visible to the wave's other lanes before any access after it, and the compiler
+// moves no memory access across it.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // One row per wave, four rows per workgroup.
 template <typename T>
 __global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ W, int d_out, int d_in,
@@ -309,11 +318,17 @@ __device__ __forceinline__ f32x4 base_tile_part(const T* __restrict__ W, int64_t
         const uint4 x = *reinterpret_cast<const uint4*>(xrow + (in ? k : 0));
         xv[u] = in ? x : make_uint4(0, 0, 0, 0);
       }
+      // the stage window passes W between lanes of this wave: each lane reads what
+      // other lanes wrote, which per-lane program order does not order, so the
+      // writes are fenced and a wave barrier keeps the compiler from moving the
+      // LDS accesses across each other (here, and before the next window's writes)
 #pragma unroll
       for (int u = 0; u < U; ++u)
         *reinterpret_cast<uint4*>(stage + (4 * u + (lane >> 4)) * kBaseLdw + 8 * (lane & 15)) = wl[u];
+      lds_wave_sync();
 #pragma unroll
       for (int u = 0; u < U; ++u) wv[u] = *reinterpret_cast<const uint4*>(stage + i * kBaseLdw + 32 * u + 8 * q);
+      lds_wave_sync();
 #pragma unroll
       for (int u = 0; u < U; ++u)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[u]),

@@ -97,13 +97,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
-__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float c) {
-  u32x4 o;
-  o.x = pack_bf16x2(bf16_lo(v.x) * c, bf16_hi(v.x) * c);
-  o.y = pack_bf16x2(bf16_lo(v.y) * c, bf16_hi(v.y) * c);
-  o.z = pack_bf16x2(bf16_lo(v.z) * c, bf16_hi(v.z) * c);
-  o.w = pack_bf16x2(bf16_lo(v.w) * c, bf16_hi(v.w) * c);
-  return o;
+// c * b for two bf16 values b packed in one word, as a pair of bf16 words: hi the
+// product rounded to bf16, lo the remainder c*b - hi (formed exactly by the fma, then
+// rounded to bf16), so hi + lo carries c*b to about 16 significant bits.
+__device__ __forceinline__ void split_bf16x2(uint32_t v, float c, uint32_t& hi, uint32_t& lo) {
+  const float b0 = bf16_lo(v), b1 = bf16_hi(v);
+  hi = pack_bf16x2(b0 * c, b1 * c);
+  lo = pack_bf16x2(fmaf(b0, c, -bf16_lo(hi)), fmaf(b1, c, -bf16_hi(hi)));
+}
+
+__device__ __forceinline__ void split_bf16x8(u32x4 v, float c, u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+  split_bf16x2(v.x, c, h[0], l[0]);
+  split_bf16x2(v.y, c, h[1], l[1]);
+  split_bf16x2(v.z, c, h[2], l[2]);
+  split_bf16x2(v.w, c, h[3], l[3]);
+  hi = (u32x4){h[0], h[1], h[2], h[3]};
+  lo = (u32x4){l[0], l[1], l[2], l[3]};
+}
+
+// Order the LDS accesses of one wave: writes before it are visible to the wave's other
+// lanes after it, and the compiler moves no memory access across it.
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Wave 0 gathers the active slots of both selections into LDS, in selection
@@ -196,9 +214,24 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 // col(ct, m) = 32 (ct / 2) + 8 (m / 4) + 4 (ct % 2) + m % 4 inside the wave's strip,
 // so lane (q, i) owns the columns 32 h + 8 q + [0, 8), h = 0 .. CT/2 - 1.
 //
-// Operands per K chunk of KC, double-buffered in LDS:
-//   Bs[row][k] = bf16(c_j * B_{e_j}[row][k - j r])   (rows of B_cat, gate folded in)
+// Operands per K chunk of KC, in NBUF LDS buffers (two: chunk c+1 is stored while
+// chunk c is multiplied; one for launches whose contraction is a single chunk):
 //   As[k][col] = A_{e_j}[k - j r][col]               (rows of A_cat, as stored)
+//   B_cat rows, in one of two forms that both carry the coefficients c_j = +-s g_j
+//   at fp32 accuracy:
+//   * split fold (every short contraction, and long ones whose rank is not a
+//     multiple of the chunk): c_j B_{e_j} as a pair of bf16 planes,
+//       Bh[row][k] = bf16(c_j b),  Bl[row][k] = bf16(c_j b - Bh[row][k]),
+//     each multiplied by A_cat on MFMA into the same accumulators, so c_j b enters
+//     the product with ~16 significant bits (a single bf16 plane, 8 bits, erred by
+//     up to 2^-8 of sum_t |c b_t a_t|, which weights that cancel a large delta feel);
+//   * scaled accumulators (long contractions whose chunks each lie in one slot):
+//     Bs[row][k] = B_{e_j}[row][k - j r] unscaled, and the slots run in order of
+//     increasing |c_j|; before the first chunk of slot j+1 the fp32 accumulators are
+//     multiplied by c_j / c_{j+1} (at most 1 in magnitude, so nothing overflows), and
+//     the epilogue multiplies the delta by the last slot's c: a Horner form of
+//     sum_j c_j (B_{e_j} A_{e_j}) with fp32 roundings only, and no fold work per
+//     gathered element.
 // A B fragment (8 consecutive k of one row) is one 16-byte LDS read.  An A fragment
 // (8 consecutive k of one column) is gathered from the row-major As with two
 // ds_read_b64_tr_b16: inside each 16-lane group, lanes 4t..4t+3 point at 16 elements
@@ -219,17 +252,21 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 //   2: any other r (division; B element by element)
 //   3: r a power of two and a multiple of KC: every chunk lies inside one slot, so the
 //      slot, its coefficient and its base addresses are uniform per chunk
-// LONG marks the long-contraction instantiation (k*r > 64: 128 x 128 tiles, 64-deep
-// chunks): it asks for two waves per SIMD and defers the gather masks (step 4).
+// LONG marks the long-contraction instantiations (k*r > 64: 128 x 128 tiles): they ask
+// for two waves per SIMD and defer the gather masks (step 4); with RMODE 3 they use
+// the scaled accumulators, otherwise the split fold.
 #ifndef ADA_WAVES_PER_EU
 #define ADA_WAVES_PER_EU 1
 #endif
-template <int KC, int RB, int CT, int WGN, int RMODE, bool LONG>
+template <int KC, int RB, int CT, int WGN, int RMODE, bool LONG, int NBUF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LONG ? 2 : ADA_WAVES_PER_EU, 8)))
 merge_bf16_kernel(MergeParams p) {
   constexpr int WGM = 4 / WGN;
   constexpr int BM = 16 * RB * WGM, BN = 16 * CT * WGN;
-  constexpr int LDB = KC + 8;   // Bs row pitch (elements)
+  constexpr bool kAccScale = LONG && RMODE == 3;  // coefficients on the fp32 accumulators
+  constexpr bool kSplit = !kAccScale;             // coefficients folded into B as a bf16 pair
+  constexpr int NPL = kSplit ? 2 : 1;             // B planes per buffer
+  constexpr int LDB = KC + 8;   // B plane row pitch (elements)
   // As row pitch: BN + 32 elements is 16 (mod 64) banks, so the 16 lanes of a
   // transposed read (4 k rows x 4 column chunks) touch 16 disjoint bank pairs; the
   // short-contraction tiles read A once per tile and keep the smaller pitch, whose
@@ -240,21 +277,24 @@ merge_bf16_kernel(MergeParams p) {
   constexpr int B_VPT = (NBV + 255) / 256;
   constexpr int A_VPT = (NAV + 255) / 256;
   static_assert(WGM * WGN == 4 && CT % 2 == 0 && NBV % 64 == 0 && NAV % 64 == 0, "tile shape");
+  static_assert(NBUF == 1 || NBUF == 2, "one or two operand buffers");
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-  // LDS: the double-buffered operand chunks, and (after the last MFMA) the fp32 delta
-  // tile in the same bytes
+  // LDS: the operand chunk buffers, and (after the last MFMA) the fp32 delta tile in
+  // the same bytes
   constexpr int LDD = BN + 4;  // delta row pitch (floats): 16 rows of a 16-byte column write hit 64 banks
-  constexpr int STAGE_BYTES = 2 * (BM * LDB + KC * LDA) * 2;
+  constexpr int BPLANE = BM * LDB;
+  constexpr int STAGE_BYTES = NBUF * (NPL * BPLANE + KC * LDA) * 2;
   constexpr int DELTA_BYTES = BM * LDD * 4;
   constexpr int SMEM = STAGE_BYTES > DELTA_BYTES ? STAGE_BYTES : DELTA_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  uint16_t (*Bs)[BM * LDB] = reinterpret_cast<uint16_t (*)[BM * LDB]>(smem);
-  uint16_t (*As)[KC * LDA] = reinterpret_cast<uint16_t (*)[KC * LDA]>(smem + 2 * BM * LDB * 2);
+  uint16_t (*Bs)[NPL * BPLANE] = reinterpret_cast<uint16_t (*)[NPL * BPLANE]>(smem);
+  uint16_t (*As)[KC * LDA] = reinterpret_cast<uint16_t (*)[KC * LDA]>(smem + NBUF * NPL * BPLANE * 2);
   float* Ds = reinterpret_cast<float*>(smem);
   __shared__ int s_exp[kMaxSlots];
   __shared__ float s_coef[kMaxSlots];
+  __shared__ float s_ratio[kAccScale ? kMaxSlots : 1];  // c_j / c_{j+1} in slot order
   __shared__ int s_n;
 
   const int tid = threadIdx.x;
@@ -321,6 +361,31 @@ merge_bf16_kernel(MergeParams p) {
       n += __popcll(m);
     }
     if (lane == 0) s_n = n;
+    if constexpr (kAccScale) {
+      // Scaled accumulators: order the slots by increasing |c| (equal magnitudes keep
+      // their order) and record the ratio of each slot's coefficient to the next one's.
+      // Every chunk here lies inside one slot of r >= KC terms, and one launch spans at
+      // most kMaxKR terms, so there are at most kMaxKR / KC <= 64 slots: one per lane.
+      // The magnitudes are compared as the integers of their bits, a total order (NaN
+      // above infinity), so the ranks are a permutation whatever the gates hold.
+      lds_wave_sync();
+      const bool mine = lane < n;
+      const int e_l = mine ? s_exp[lane] : 0;
+      const float c_l = mine ? s_coef[lane] : 0.f;
+      const uint32_t a_l = __float_as_uint(c_l) & 0x7fffffffu;
+      int rank = 0;
+      for (int i = 0; i < n; ++i) {
+        const uint32_t a_i = __float_as_uint(s_coef[i]) & 0x7fffffffu;
+        rank += (a_i < a_l || (a_i == a_l && i < lane)) ? 1 : 0;
+      }
+      lds_wave_sync();
+      if (mine) {
+        s_exp[rank] = e_l;
+        s_coef[rank] = c_l;
+      }
+      lds_wave_sync();
+      if (lane + 1 < n) s_ratio[lane] = s_coef[lane] / s_coef[lane + 1];
+    }
   }
   __syncthreads();
   const int nslot = s_n;
@@ -358,6 +423,7 @@ merge_bf16_kernel(MergeParams p) {
   // A k row v / (BN/8), columns 8 (v % (BN/8)).  Threads past the vector count (whole
   // waves, as the counts are multiples of 64) skip.
   u32x4 sb[B_VPT];
+  u32x4 sbl[B_VPT];  // RMODE 2: the lo plane, split at the load
   float sc[B_VPT];
   u32x4 sa[A_VPT];
   // Long contractions apply the in-range masks in stage_store: applied at the load,
@@ -389,7 +455,7 @@ merge_bf16_kernel(MergeParams p) {
       const int j = k0 >> r_shift;  // < nslot: the chunks tile the contraction exactly
       const int rr0 = k0 & (r - 1);
       const int e = __builtin_amdgcn_readfirstlane(s_exp[j]);
-      const float c = s_coef[j];
+      const float c = kSplit ? s_coef[j] : 1.f;
       const ADA_GLOBAL unsigned char* bj = gB + 2u * (uint32_t(e) * uint32_t(T.d_out) * uint32_t(r) + uint32_t(rr0));
       const ADA_GLOBAL unsigned char* aj = gA + 2u * ((uint32_t(e) * uint32_t(r) + uint32_t(rr0)) * uint32_t(T.d_in));
 #pragma unroll
@@ -428,20 +494,25 @@ merge_bf16_kernel(MergeParams p) {
         sb[i] = kDefer ? val : (val & (u32x4)sbm[i]);
         sc[i] = s_coef[js];
       } else {
-        // rank not a multiple of 8: element by element, coefficient applied here
-        uint32_t w[4] = {0, 0, 0, 0};
+        // rank not a multiple of 8: element by element, the coefficient applied and
+        // the product split into its two bf16 planes here
+        uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           int j, rr;
           split(k0 + 8 * kv + t, j, rr);
-          float x = 0.f;
-          if (j < nslot && grow < T.d_out)
-            x = __uint_as_float(uint32_t(gB16[(int64_t(s_exp[j]) * T.d_out + grow) * r + rr]) << 16) *
-                s_coef[j];
-          const uint32_t hb = pack_bf16x2(x, 0.f) & 0xffffu;
-          w[t >> 1] |= hb << (16 * (t & 1));
+          float b = 0.f, c = 0.f;
+          if (j < nslot && grow < T.d_out) {
+            b = __uint_as_float(uint32_t(gB16[(int64_t(s_exp[j]) * T.d_out + grow) * r + rr]) << 16);
+            c = s_coef[j];
+          }
+          const uint32_t hb = pack_bf16x2(b * c, 0.f) & 0xffffu;
+          const uint32_t lb = pack_bf16x2(fmaf(b, c, -bf16_lo(hb)), 0.f) & 0xffffu;
+          wh[t >> 1] |= hb << (16 * (t & 1));
+          wl[t >> 1] |= lb << (16 * (t & 1));
         }
-        sb[i] = (u32x4){w[0], w[1], w[2], w[3]};
+        sb[i] = (u32x4){wh[0], wh[1], wh[2], wh[3]};
+        sbl[i] = (u32x4){wl[0], wl[1], wl[2], wl[3]};
         sbm[i] = ~0u;
         sc[i] = 1.f;
       }
@@ -475,10 +546,18 @@ merge_bf16_kernel(MergeParams p) {
       // column 0, whose products reach only output rows or columns never stored;
       // short tiles were masked at the load)
       const u32x4 v8 = (RMODE == 3 || !kDefer) ? sb[i] : (sb[i] & (u32x4)sbm[i]);
-      if constexpr (rvec)
-        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = scale_bf16x8(v8, sc[i]);
-      else
-        *reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]) = v8;
+      u32x4* bh = reinterpret_cast<u32x4*>(&Bs[buf][row * LDB + 8 * kv]);
+      if constexpr (kAccScale) {
+        *bh = v8;
+      } else if constexpr (rvec) {
+        u32x4 hi, lo;
+        split_bf16x8(v8, sc[i], hi, lo);
+        bh[0] = hi;
+        *reinterpret_cast<u32x4*>(&Bs[buf][BPLANE + row * LDB + 8 * kv]) = lo;
+      } else {
+        bh[0] = v8;
+        *reinterpret_cast<u32x4*>(&Bs[buf][BPLANE + row * LDB + 8 * kv]) = sbl[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < A_VPT; ++i) {
@@ -510,7 +589,8 @@ merge_bf16_kernel(MergeParams p) {
 
   // 4. chunk 0, then the pipelined K loop (one barrier per chunk: chunk c+1 is
   // written to the other buffer, which every wave finished reading at the previous
-  // barrier).
+  // barrier).  With the split fold every B fragment is multiplied twice, hi plane
+  // first for all blocks, then the lo plane, so dependent MFMAs are RB*CT apart.
   auto mfma_chunk = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < KC / 32; ++ks) {
@@ -532,12 +612,45 @@ merge_bf16_kernel(MergeParams p) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
           acc[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ct], bfr[rb], acc[rb][ct], 0, 0, 0);
+      if constexpr (kSplit) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          bfr[rb] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][BPLANE + boff[rb] + 32 * ks]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ct], bfr[rb], acc[rb][ct], 0, 0, 0);
+      }
+    }
+  };
+  // Scaled accumulators: entering chunk c + 1, which starts slot j + 1 when
+  // (c + 1) KC is a multiple of r, multiply by c_j / c_{j+1}.
+  auto rescale = [&](int c) {
+    if constexpr (kAccScale) {
+      const int k1 = (c + 1) * KC;
+      if ((k1 & (r - 1)) == 0) {
+        const float rho = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_ratio[(k1 >> r_shift) - 1])));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            acc[rb][ct][0] *= rho;
+            acc[rb][ct][1] *= rho;
+            acc[rb][ct][2] *= rho;
+            acc[rb][ct][3] *= rho;
+          }
+      }
     }
   };
   stage_load(0);
   stage_store(0);
   __syncthreads();
-  if constexpr (kDefer) {
+  if constexpr (NBUF == 1) {
+    // the launch's contraction fits one chunk (the host picks this form only then)
+    mfma_chunk(0);
+  } else if constexpr (kDefer) {
     // Long contractions: the last chunk is peeled off the loop, so every gather
     // issued in the loop body is consumed in the same body (a load that could still
     // be pending at the loop exit would make the compiler wait on it in the
@@ -551,6 +664,7 @@ merge_bf16_kernel(MergeParams p) {
       mfma_chunk(buf);
       __builtin_amdgcn_sched_barrier(0);
       stage_store(buf ^ 1);
+      rescale(c);
       __syncthreads();
     }
     mfma_chunk((nchunks - 1) & 1);
@@ -569,7 +683,9 @@ merge_bf16_kernel(MergeParams p) {
 
   // 5. delta through LDS into the row-major layout of the W vectors: lane (q, i) of
   //    block (rb, ct) holds 4 adjacent columns of one row (a 16-byte write); then
-  //    W + delta is rounded once and stored
+  //    W + delta is rounded once and stored (with scaled accumulators the delta is
+  //    first multiplied by the last slot's coefficient, in the same fma)
+  const float cl = kAccScale ? s_coef[nslot - 1] : 1.f;
   __syncthreads();  // every wave is done reading the operand chunks the delta overwrites
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -589,10 +705,17 @@ merge_bf16_kernel(MergeParams p) {
     const f32x4 d1 = *reinterpret_cast<const f32x4*>(d + 4);
     const u32x4 w = wv[u];
     u32x4 o;
-    o.x = pack_bf16x2(bf16_lo(w.x) + d0[0], bf16_hi(w.x) + d0[1]);
-    o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
-    o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
-    o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
+    if constexpr (kAccScale) {
+      o.x = pack_bf16x2(fmaf(d0[0], cl, bf16_lo(w.x)), fmaf(d0[1], cl, bf16_hi(w.x)));
+      o.y = pack_bf16x2(fmaf(d0[2], cl, bf16_lo(w.y)), fmaf(d0[3], cl, bf16_hi(w.y)));
+      o.z = pack_bf16x2(fmaf(d1[0], cl, bf16_lo(w.z)), fmaf(d1[1], cl, bf16_hi(w.z)));
+      o.w = pack_bf16x2(fmaf(d1[2], cl, bf16_lo(w.w)), fmaf(d1[3], cl, bf16_hi(w.w)));
+    } else {
+      o.x = pack_bf16x2(bf16_lo(w.x) + d0[0], bf16_hi(w.x) + d0[1]);
+      o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
+      o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
+      o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
+    }
     store16_stream(dst, woff[u], o);
   }
 }
@@ -683,16 +806,16 @@ __global__ void __launch_bounds__(256) merge_f32_kernel(MergeParams p) {
   }
 }
 
-template <int KC, class S, bool LONG>
+template <int KC, class S, bool LONG, int NBUF>
 void launch_bf16(const MergeParams& p, dim3 grid, dim3 block, hipStream_t s) {
   if (p.r_shift >= 0 && p.r % KC == 0)
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 3, LONG>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 3, LONG, NBUF>), grid, block, 0, s, p);
   else if (p.r_shift >= 0 && (p.r & 7) == 0)
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 0, LONG>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 0, LONG, NBUF>), grid, block, 0, s, p);
   else if ((p.r & 7) == 0)
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 1, LONG>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 1, LONG, NBUF>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 2, LONG>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((merge_bf16_kernel<KC, S::rb, S::ct, S::wgn, 2, LONG, NBUF>), grid, block, 0, s, p);
 }
 
 }  // namespace
@@ -704,10 +827,20 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t
     // the caller built p's work table for the tile class of kr_max
     // short contractions loop over 32-deep chunks (a 64-deep chunk costs a wave per
     // SIMD in registers: the fused switch at k*r = 64 ran 30% slower with it)
+    // k*r <= 32 is a single chunk (one operand buffer); long contractions whose rank is a
+    // power-of-two multiple of 64 run 64-deep chunks, one slot each, on scaled
+    // accumulators, and the other long ones 32-deep chunks (scaled accumulators again
+    // at rank 32; otherwise the split fold, whose second B plane needs the room)
     switch (bf16_tile_class(kr_max)) {
-      case 0: launch_bf16<32, NarrowTile, false>(p, grid, block, s); break;
-      case 1: launch_bf16<32, ShortTile, false>(p, grid, block, s); break;
-      default: launch_bf16<64, LongTile, true>(p, grid, block, s); break;
+      case 0: launch_bf16<32, NarrowTile, false, 1>(p, grid, block, s); break;
+      case 1: launch_bf16<32, ShortTile, false, 2>(p, grid, block, s); break;
+      default:
+        if (p.r_shift >= 0 && p.r % 64 == 0)
+          hipLaunchKernelGGL((merge_bf16_kernel<64, LongTile::rb, LongTile::ct, LongTile::wgn, 3, true, 2>), grid,
+                             block, 0, s, p);
+        else
+          launch_bf16<32, LongTile, true, 2>(p, grid, block, s);
+        break;
     }
   } else {
     hipLaunchKernelGGL(merge_f32_kernel<32>, grid, block, 0, s, p);

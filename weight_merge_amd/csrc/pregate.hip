@@ -31,9 +31,11 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
-// Order-preserving map of fp32 bits to uint32 (larger float -> larger key).
+// Order-preserving map of fp32 bits to uint32 (larger float -> larger key).  -0.0
+// and +0.0 are equal scores, so both map to the key of +0.0 (the tie then goes to the
+// lower index, as for any other pair of equal scores).
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
+  const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
