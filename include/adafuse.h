@@ -216,6 +216,22 @@ int ada_lora_layer(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_
                    void* workspace, int64_t workspace_bytes, int32_t dtype, void* stream);
 
 /*
+ * ada_lora_layer without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the fp32 intermediates live in a static device array inside the
+ * library, 4 MiB per GPU, which each GPU the library runs on holds until the process
+ * ends.  The call allocates nothing; it returns ADA_ESHAPE (before any HIP call) when
+ * the layer needs more than 4 MiB of intermediates (4 * sum_p roundup4(d_out_p + k*r)
+ * bytes > 4 MiB), and otherwise computes exactly what ada_lora_layer computes.  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other host threads) race, so order them.  The array's contents are
+ * left from the last call; every element a call reads it has written first.
+ */
+int ada_lora_layer_static(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_t r,
+                          const int32_t* idx, const float* gate, int32_t k, float scale,
+                          int32_t dtype, void* stream);
+
+/*
  * A batch of nb requests (1 <= nb <= 16), each with its OWN selection, through one
  * layer of the unmerged routed path, in two launches.  The pages treat batch-1
  * requests with one selection each; a merged backbone can hold only one selection,

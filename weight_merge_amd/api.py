@@ -256,15 +256,9 @@ def lora_layer_workspace_elems(d_outs, k: int, r: int) -> int:
     return n
 
 
-def ada_lora_layer(projs, idx, gate, scale: float, workspace=None, stream=None):
-    """One layer of the unmerged routed path (two launches for all projections).
-
-    projs: list of (w, a, b, x, y) with w [d_out, d_in], a [E, r, d_in], b [E, d_out, r],
-    x [d_in], y [d_out] (written)."""
-    projs = list(projs)
+def _lora_layer_projs(projs):
     w0, a0 = projs[0][0], projs[0][1]
     E, r, _ = a0.shape
-    pi, pg, k = _sel(idx, gate)
     arr = (AdaLoraProj * len(projs))()
     for i, (w, a, b, x, y) in enumerate(projs):
         d_out, d_in = w.shape
@@ -278,6 +272,17 @@ def ada_lora_layer(projs, idx, gate, scale: float, workspace=None, stream=None):
             raise TypeError("all tensors share one dtype")
         arr[i] = AdaLoraProj(_dev(w, "w"), _dev(a, "a"), _dev(b, "b"), _dev(x, "x"), _dev(y, "y"), d_out, d_in,
                              w.stride(0))
+    return arr, w0, E, r
+
+
+def ada_lora_layer(projs, idx, gate, scale: float, workspace=None, stream=None):
+    """One layer of the unmerged routed path (two launches for all projections).
+
+    projs: list of (w, a, b, x, y) with w [d_out, d_in], a [E, r, d_in], b [E, d_out, r],
+    x [d_in], y [d_out] (written)."""
+    projs = list(projs)
+    arr, w0, E, r = _lora_layer_projs(projs)
+    pi, pg, k = _sel(idx, gate)
     need = lora_layer_workspace_elems([p[0].shape[0] for p in projs], k, r)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.float32, device=w0.device)
@@ -285,6 +290,17 @@ def ada_lora_layer(projs, idx, gate, scale: float, workspace=None, stream=None):
     st = _lib.load().ada_lora_layer(arr, len(projs), E, r, pi, pg, k, float(scale), _dev(workspace, "workspace"),
                                     workspace.numel() * workspace.element_size(), _dtype(w0), _stream(stream))
     _check(st, "ada_lora_layer")
+
+
+def ada_lora_layer_static(projs, idx, gate, scale: float, stream=None):
+    """ada_lora_layer with its intermediates in the library's static device array (4 MiB
+    per GPU): the C call allocates nothing.  Calls overlapping in time on one GPU race."""
+    projs = list(projs)
+    arr, w0, E, r = _lora_layer_projs(projs)
+    pi, pg, k = _sel(idx, gate)
+    st = _lib.load().ada_lora_layer_static(arr, len(projs), E, r, pi, pg, k, float(scale), _dtype(w0),
+                                           _stream(stream))
+    _check(st, "ada_lora_layer_static")
 
 
 def lora_batch_workspace_elems(d_outs, nb: int, k: int, r: int) -> int:

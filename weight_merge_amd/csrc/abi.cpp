@@ -140,6 +140,55 @@ int check_selection(const ada_model_s* m, const int32_t* idx, const float* gate,
   return ADA_OK;
 }
 
+// Checks and launch parameters of one layer of the unmerged routed path (everything but
+// the fp32 intermediates' address); ws_bytes is the space those intermediates need.
+int prepare_lora_layer(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_t r, const int32_t* idx,
+                       const float* gate, int32_t k, float scale, int32_t dtype, ada::LoraLayerParams& p,
+                       int64_t& dot_rows, int64_t& out_rows, int64_t& ws_bytes) {
+  if (projs == nullptr || idx == nullptr || gate == nullptr) return ADA_EINVAL;
+  if (!dtype_ok(dtype)) return ADA_EDTYPE;
+  if (!aligned4(idx) || !aligned4(gate)) return ADA_EALIGN;
+  if (n_proj < 1 || n_proj > ada::kMaxLayerProj) return ADA_ESHAPE;
+  if (E < 1 || E > 64 || r < 1 || k < 1 || k > E || int64_t(k) * r > ada::kMaxKR) return ADA_ESHAPE;
+  const int esz = dtype == ADA_BF16 ? 2 : 4;
+  int64_t ws = 0;
+  dot_rows = out_rows = 0;
+  for (int32_t i = 0; i < n_proj; ++i) {
+    const ada_lora_proj& q = projs[i];
+    if (q.w == nullptr || q.a == nullptr || q.b == nullptr || q.x == nullptr || q.y == nullptr) return ADA_EINVAL;
+    if (!aligned16(q.w) || !aligned16(q.a) || !aligned16(q.b) || !aligned16(q.x) || !aligned16(q.y))
+      return ADA_EALIGN;
+    if (!dim_ok(q.d_out) || !dim_ok(q.d_in) || q.ld_w < q.d_in || q.ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
+    if ((q.ld_w * esz) % 16 != 0) return ADA_EALIGN;
+    ada::LoraLayerProj& P = p.proj[i];
+    P.w = q.w;
+    P.a = q.a;
+    P.b = q.b;
+    P.x = q.x;
+    P.y = q.y;
+    P.ld = q.ld_w;
+    P.d_out = q.d_out;
+    P.d_in = q.d_in;
+    P.dot_row0 = static_cast<int32_t>(dot_rows);
+    P.out_row0 = static_cast<int32_t>(out_rows);
+    P.ws_off = ws;
+    dot_rows += q.d_out + int64_t(k) * r;
+    out_rows += q.d_out;
+    ws = (ws + q.d_out + int64_t(k) * r + 3) & ~int64_t(3);  // keep every block 16-byte aligned
+  }
+  if (dot_rows >= (int64_t(1) << 30)) return ADA_ESHAPE;
+  p.n = n_proj;
+  p.E = E;
+  p.r = r;
+  p.k = k;
+  p.idx = idx;
+  p.gate = gate;
+  p.scale = scale;
+  p.nb = 1;
+  ws_bytes = ws * 4;
+  return ADA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,48 +426,31 @@ int ada_lora_apply(const void* w, int32_t d_out, int32_t d_in, int64_t ld_w, con
 int ada_lora_layer(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_t r, const int32_t* idx,
                    const float* gate, int32_t k, float scale, void* workspace, int64_t workspace_bytes,
                    int32_t dtype, void* stream) {
-  if (projs == nullptr || idx == nullptr || gate == nullptr || workspace == nullptr) return ADA_EINVAL;
-  if (!dtype_ok(dtype)) return ADA_EDTYPE;
-  if (!aligned4(idx) || !aligned4(gate) || !aligned16(workspace)) return ADA_EALIGN;
-  if (n_proj < 1 || n_proj > ada::kMaxLayerProj) return ADA_ESHAPE;
-  if (E < 1 || E > 64 || r < 1 || k < 1 || k > E || int64_t(k) * r > ada::kMaxKR) return ADA_ESHAPE;
-  const int esz = dtype == ADA_BF16 ? 2 : 4;
+  if (workspace == nullptr) return ADA_EINVAL;
+  if (!aligned16(workspace)) return ADA_EALIGN;
   ada::LoraLayerParams p{};
-  int64_t dot_rows = 0, out_rows = 0, ws = 0;
-  for (int32_t i = 0; i < n_proj; ++i) {
-    const ada_lora_proj& q = projs[i];
-    if (q.w == nullptr || q.a == nullptr || q.b == nullptr || q.x == nullptr || q.y == nullptr) return ADA_EINVAL;
-    if (!aligned16(q.w) || !aligned16(q.a) || !aligned16(q.b) || !aligned16(q.x) || !aligned16(q.y))
-      return ADA_EALIGN;
-    if (!dim_ok(q.d_out) || !dim_ok(q.d_in) || q.ld_w < q.d_in || q.ld_w > (int64_t(1) << 40)) return ADA_ESHAPE;
-    if ((q.ld_w * esz) % 16 != 0) return ADA_EALIGN;
-    ada::LoraLayerProj& P = p.proj[i];
-    P.w = q.w;
-    P.a = q.a;
-    P.b = q.b;
-    P.x = q.x;
-    P.y = q.y;
-    P.ld = q.ld_w;
-    P.d_out = q.d_out;
-    P.d_in = q.d_in;
-    P.dot_row0 = static_cast<int32_t>(dot_rows);
-    P.out_row0 = static_cast<int32_t>(out_rows);
-    P.ws_off = ws;
-    dot_rows += q.d_out + int64_t(k) * r;
-    out_rows += q.d_out;
-    ws = (ws + q.d_out + int64_t(k) * r + 3) & ~int64_t(3);  // keep every block 16-byte aligned
-  }
-  if (dot_rows >= (int64_t(1) << 30)) return ADA_ESHAPE;
-  if (workspace_bytes < ws * 4) return ADA_ESHAPE;
-  p.n = n_proj;
-  p.E = E;
-  p.r = r;
-  p.k = k;
-  p.idx = idx;
-  p.gate = gate;
-  p.scale = scale;
+  int64_t dot_rows = 0, out_rows = 0, ws_bytes = 0;
+  if (int st = prepare_lora_layer(projs, n_proj, E, r, idx, gate, k, scale, dtype, p, dot_rows, out_rows, ws_bytes);
+      st != ADA_OK)
+    return st;
+  if (workspace_bytes < ws_bytes) return ADA_ESHAPE;
   p.ws = static_cast<float*>(workspace);
-  p.nb = 1;
+  const hipError_t e = ada::launch_lora_layer(p, static_cast<int>(dot_rows), static_cast<int>(out_rows), dtype,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : ADA_EHIP;
+}
+
+int ada_lora_layer_static(const ada_lora_proj* projs, int32_t n_proj, int32_t E, int32_t r, const int32_t* idx,
+                          const float* gate, int32_t k, float scale, int32_t dtype, void* stream) {
+  ada::LoraLayerParams p{};
+  int64_t dot_rows = 0, out_rows = 0, ws_bytes = 0;
+  if (int st = prepare_lora_layer(projs, n_proj, E, r, idx, gate, k, scale, dtype, p, dot_rows, out_rows, ws_bytes);
+      st != ADA_OK)
+    return st;
+  if (ws_bytes > static_cast<int64_t>(ada::kStaticScratchBytes)) return ADA_ESHAPE;
+  void* scratch = nullptr;  // this device's copy of the library's static array (no allocation)
+  if (ada::static_scratch(&scratch) != hipSuccess) return ADA_EHIP;
+  p.ws = static_cast<float*>(scratch);
   const hipError_t e = ada::launch_lora_layer(p, static_cast<int>(dot_rows), static_cast<int>(out_rows), dtype,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ADA_OK : ADA_EHIP;

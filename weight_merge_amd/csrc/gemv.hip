@@ -13,6 +13,8 @@
 // y = RNE(y32 + s * sum_j g_j B_j t_j).
 #include "launch.h"
 
+#include <mutex>
+
 namespace ada {
 namespace {
 
@@ -462,6 +464,34 @@ hipError_t launch_lora_expand(const void* b, int E, int r, int d_out, const int3
     hipLaunchKernelGGL(lora_expand_kernel<float>, grid, block, 0, s, static_cast<const float*>(b), E, r,
                        d_out, idx, gate, k, scale, y32, t, static_cast<float*>(y));
   return hipGetLastError();
+}
+
+// ---- device memory for the allocation-free layer path (ada_lora_layer_static): a
+// file-scope array, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): it takes each device's address once, with that device current, and uses
+// that address.
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* addr = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+    g_scratch_ptr[dev] = addr;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s) {

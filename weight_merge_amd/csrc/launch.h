@@ -67,6 +67,11 @@ struct LoraLayerParams {
 };
 hipError_t launch_lora_layer(const LoraLayerParams& p, int dot_rows, int out_rows, int dtype, hipStream_t s);
 
+// The allocation-free layer path's device memory: a file-scope array of this many bytes
+// per GPU, and its address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+hipError_t static_scratch(void** ptr);
+
 // A batch of requests with a selection each, one group of projections (the unmerged
 // path serving mixed selections).  Per projection x is [nb][d_in], y [nb][d_out];
 // dot_row0 counts workgroups of the first grid: ceil(d_out / 16) base workgroups (16 W
