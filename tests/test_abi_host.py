@@ -222,3 +222,19 @@ def test_decode_gemv_layer_validation(lib):
     assert f(arr(d_in=60), 1, ADA_BF16, None) == ADA_ESHAPE
     assert f(arr(ld_w=32), 1, ADA_BF16, None) == ADA_ESHAPE
     assert f(arr(ld_w=68), 1, ADA_BF16, None) == ADA_EALIGN
+
+
+def test_model_create_builds_its_tables_before_the_first_hip_call(lib):
+    """Valid stacks (many ragged projections, strided rows, one tiny and one at the
+    size limits) pass validation and the host-side table build; with no GPU visible
+    the first HIP call then fails, so the call returns ADA_EHIP and allocates nothing."""
+    shapes = [(8, 8), (264, 520), (4096, 11008), (11008, 4096), (136, 8), (8, 4096)]
+    projs = [proj(d_out=do, d_in=di, ld_w=di + 8 * (i % 3)) for i, (do, di) in enumerate(shapes)]
+    edge = projs + [proj(d_out=1 << 22, d_in=8, ld_w=8), proj(d_out=8, d_in=1 << 22, ld_w=1 << 22)]  # E r 2^22 < 2^31
+    for dt in (ADA_F32, ADA_BF16):
+        for E, r in ((1, 1), (8, 16), (16, 64), (64, 8)):
+            assert create(lib, projs, E=E, r=r, dt=dt) == _lib.ADA_EHIP
+        for E, r in ((1, 1), (8, 16)):
+            assert create(lib, edge, E=E, r=r, dt=dt) == _lib.ADA_EHIP
+    many = [proj(d_out=8 * (1 + i % 40), d_in=8 * (1 + (7 * i) % 50), ld_w=400) for i in range(3000)]
+    assert create(lib, many, E=8, r=16, dt=ADA_BF16) == _lib.ADA_EHIP
