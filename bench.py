@@ -151,13 +151,13 @@ def write_traffic(args, cfg, out=None):
         "#",
         "# Commands (each a pass of its own, run from the repository root on one MI355X):",
         "#   export TMPDIR=/tmp",
-        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fdir} -o f -- python3 bench.py --steps 2 "
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fdir} -o p -- python3 bench.py --steps 2 "
         f"--warmup 1 --no-cpu-baseline --no-copy-ceiling --extra ''{flags}",
-        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wdir} -o w -- python3 bench.py --steps 2 "
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {wdir} -o p -- python3 bench.py --steps 2 "
         f"--warmup 1 --no-cpu-baseline --no-copy-ceiling --extra ''{flags}",
-        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfdir} -o f -- python3 bench.py "
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfdir} -o p -- python3 bench.py "
         f"--calibrate-copy {args.calibrate_mib}",
-        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwdir} -o w -- python3 bench.py "
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwdir} -o p -- python3 bench.py "
         f"--calibrate-copy {args.calibrate_mib}",
         f"#   python3 bench.py{flags} --traffic-from {fdir} {wdir} {cfdir} {cwdir} --calibrate-mib {args.calibrate_mib}",
         f"# Counter values are the mean per dispatch of the named kernel ({nf} / {nw} {kname} dispatches: merges "
