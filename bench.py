@@ -68,6 +68,9 @@ def parse():
                          "command line's workload found under DIR, the timed launches averaged apart from the "
                          "warm-up ones, and exit; needs no GPU")
     ap.add_argument("--trace-command", default="", help="the profiled command, quoted in the trace summary")
+    ap.add_argument("--counter-summary", nargs="+", metavar="X",
+                    help="OUT DIR [DIR ...]: write a markdown table (OUT, under profiles/) of every counter found "
+                         "in the rocprofv3 --pmc output folders DIR, the mean per merge-kernel dispatch, and exit")
     return ap.parse_args()
 
 
@@ -601,6 +604,8 @@ def trace_summary(args, cfg):
     if not rows:
         raise SystemExit(f"no kernel_trace.csv under {folder}")
     rows.sort()
+    if cfg.decode_steps:
+        return decode_trace_summary(args, cfg, rows, folder, out)
     agent = "gfx950"
     stats = {}
     for t0, t1, name in rows:
@@ -649,6 +654,97 @@ def trace_summary(args, cfg):
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out}: timed merge mean {mean_t:.1f} µs ({alg / mean_t / 1e3:.0f} GB/s)")
+
+
+def decode_trace_summary(args, cfg, rows, folder, out):
+    """The end-to-end run's kernel table, and the decode GEMV launches split by group of
+    projections: every path launches one gemv_layer_kernel per group, in the order
+    {q, k, v}, {o}, {gate, up}, {down}, so the i-th launch belongs to group i mod 4."""
+    stats = {}
+    for t0, t1, name in rows:
+        k = kernel_short_name(name)
+        c, tot = stats.get(k, (0, 0.0))
+        stats[k] = (c + 1, tot + (t1 - t0) / 1e3)
+    grand = sum(t for _, t in stats.values())
+    names = [p.name for p in cfg.projections]
+    order = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    gbytes = [sum(cfg.projections[names.index(n)].d_out * cfg.projections[names.index(n)].d_in * cfg.elem_bytes
+                  for n in g) for g in order]
+    gemv = [(t1 - t0) / 1e3 for t0, t1, n in rows if "gemv_layer_kernel" in n]
+    lines = [
+        f"# rocprofv3 kernel trace: end-to-end request on `{cfg.name}` ({cfg.note})",
+        "",
+        "Command (from the repository root on one MI355X), and the summary's own command:",
+        "",
+        "```",
+        f"export TMPDIR=/tmp; {args.trace_command}",
+        f"python3 bench.py --workload {cfg.name} --steps {args.steps} --trace-summary {folder} {out}",
+        "```",
+        "",
+        "| kernel | calls | total µs | avg µs | % |",
+        "|---|---|---|---|---|",
+    ]
+    for k, (c, tot) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| `{k[:90]}` | {c} | {tot:.1f} | {tot / c:.2f} | {100 * tot / grand:.1f} |")
+    lines += ["", "Decode GEMV launches (`gemv_layer_kernel`) by group of projections (every decode path of the run):",
+              "", "| group | launches | bytes per launch | avg µs | GB/s |", "|---|---|---|---|---|"]
+    for i, (g, b) in enumerate(zip(order, gbytes)):
+        d = gemv[i::4]
+        if d:
+            m = sum(d) / len(d)
+            lines.append(f"| {', '.join(g)} | {len(d)} | {b:,} | {m:.2f} | {b / m / 1e3:.0f} |")
+    if gemv:
+        per_tok = sum(sum(gemv[i::4]) / max(1, len(gemv[i::4])) for i in range(4)) * cfg.n_layers
+        lines.append(f"\nOne token ({cfg.n_layers} layers x 4 launches) at these averages: {per_tok / 1e3:.3f} ms, "
+                     f"{cfg.decode_bytes_per_token() / per_tok / 1e3:.0f} GB/s.")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
+def counter_summary(args, cfg):
+    """Markdown table of the rocprofv3 --pmc passes in the given folders: for every
+    counter, the mean per dispatch of the merge kernel (summed over the chip)."""
+    import csv
+    import glob
+
+    out, folders = args.counter_summary[0], args.counter_summary[1:]
+    vals, names = {}, set()
+    for d in folders:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if "merge_bf16_kernel" not in row["Kernel_Name"] and "merge_f32_kernel" not in row["Kernel_Name"]:
+                        continue
+                    disp = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                    key = (row["Counter_Name"], d)
+                    tot = vals.setdefault(key, {})
+                    tot[disp] = tot.get(disp, 0.0) + float(row["Counter_Value"])
+                    names.add(kernel_short_name(row["Kernel_Name"]))
+    if not vals:
+        raise SystemExit(f"no merge-kernel counters under {folders}")
+    lines = [
+        f"# rocprofv3 counters: merge kernel on `{cfg.name}` ({cfg.note})",
+        "",
+        "Commands (from the repository root on one MI355X; one pass per folder, counters as listed):",
+        "",
+        "```",
+        f"export TMPDIR=/tmp; {args.trace_command}",
+        f"python3 bench.py --workload {cfg.name} --counter-summary {' '.join(args.counter_summary)}",
+        "```",
+        "",
+        f"Kernel: {', '.join(f'`{n}`' for n in sorted(names))}; merge kernel code hash (bench.py kernel_sha, comments "
+        f"aside): {kernel_sha()}.  Each value is the mean over the pass's merge-kernel dispatches (merges and "
+        "unmerges) of the counter summed over the chip.",
+        "",
+        "| counter | per dispatch | dispatches | pass |",
+        "|---|---|---|---|",
+    ]
+    for (cname, d), per in sorted(vals.items()):
+        lines.append(f"| {cname} | {sum(per.values()) / len(per):,.0f} | {len(per)} | `{os.path.basename(d)}` |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}: {len(vals)} counters")
 
 
 def time_merge_workload(cfg, args, torch, A, synth, dev, steps, warmup, out_of_place):
@@ -725,6 +821,8 @@ def main():
         return write_traffic(args, PRESETS[args.workload])
     if args.trace_summary:
         return trace_summary(args, PRESETS[args.workload])
+    if args.counter_summary:
+        return counter_summary(args, PRESETS[args.workload])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the merge needs no communication between GPUs (each merges "

@@ -121,11 +121,15 @@ int ada_pregate(const void* h, const void* router, int32_t d, int32_t E, int32_t
  * Fused merge of the selected adapters into every registered projection in ONE
  * kernel launch ([pt] 2.B; [ja] 2.2):
  *   w_out (or w in place) = RNE(w + sum_j scale*gate[j] * B[idx[j]] @ A[idx[j]]).
- * idx, gate: device arrays of k entries (as written by ada_pregate).  Slots whose
- * gate is 0 are skipped; if every gate is 0 an in-place merge writes nothing and
- * an out-of-place merge copies w.  Indices outside [0, E) are skipped.  The
- * caller keeps (idx, gate, scale) to unmerge.  Overlapping calls on one model's
- * weights race.  k*r <= 512.
+ * Each coefficient scale*gate[j] is applied at fp32 accuracy and products are
+ * summed in fp32, so the result is the exact merge rounded once to the storage type
+ * (to within fp32 accumulation).  idx, gate: device arrays of k entries (as written
+ * by ada_pregate).  Slots whose gate is 0 are skipped; if every gate is 0 an
+ * in-place merge writes nothing and an out-of-place merge copies w.  Indices outside
+ * [0, E) are skipped.  The caller keeps (idx, gate, scale) to unmerge.  On an
+ * out-of-place model every call reads the untouched w, so calling it again with a
+ * new selection is a drift-free switch.  Overlapping calls on one model's weights
+ * race.  k*r <= 512.
  */
 int ada_merge(ada_model m, const int32_t* idx, const float* gate, int32_t k,
               float scale, void* stream);
@@ -144,6 +148,14 @@ int ada_unmerge(ada_model m, const int32_t* idx, const float* gate, int32_t k,
  * Fused switch between selections ([pt] 2.B: undo the previous token's fusion and
  * apply the current one in one pass): buffer = RNE(buffer - delta(prev) + delta(cur)),
  * one read and one write of every weight.  (k_prev + k_cur) * r <= 512.
+ * Drift: every switch rounds the buffer to bf16 again, so a chain of switches moves
+ * away from W + delta(cur).  From a fresh merge one switch stays within the stated
+ * tolerance (8e-3 |ref| + 1e-4); measured on a 512 x 4096 projection (rank 16, top-2),
+ * 0.001% of weights are outside it after 2 switches, 1% after 8 and 11% after 31.
+ * Per-token switching without drift: register the model out of place (w_out != w)
+ * and call ada_merge for each new selection, which reads the untouched w and writes
+ * w_out (the same one read and one write per weight).  In-place models that switch
+ * must restore w from pristine weights before the second switch.
  */
 int ada_switch(ada_model m, const int32_t* idx_prev, const float* gate_prev, int32_t k_prev,
                const int32_t* idx_cur, const float* gate_cur, int32_t k_cur, float scale,

@@ -90,3 +90,17 @@ def test_trace_summary_separates_timed_from_warm_up_launches(tmp_path):
     args.warmup = 2  # a count that does not match the trace is refused
     with pytest.raises(SystemExit):
         bench.trace_summary(args, PRESETS["llama7b_e8r16k2"])
+
+
+def test_counter_summary_averages_per_dispatch(tmp_path):
+    merge = "void ada::(anonymous namespace)::merge_bf16_kernel<64, 4, 4, 2, 3, true, 2>(ada::MergeParams)"
+    d = str(tmp_path / "q1")
+    # two dispatches, each counter reported per XCD (two rows summed per dispatch)
+    _csv(d, [{"Dispatch_Id": 1, "Kernel_Name": merge, "Counter_Name": "SQ_WAVES", "Counter_Value": 10},
+             {"Dispatch_Id": 1, "Kernel_Name": merge, "Counter_Name": "SQ_WAVES", "Counter_Value": 20},
+             {"Dispatch_Id": 2, "Kernel_Name": merge, "Counter_Name": "SQ_WAVES", "Counter_Value": 50},
+             {"Dispatch_Id": 3, "Kernel_Name": "other", "Counter_Name": "SQ_WAVES", "Counter_Value": 999}])
+    out = str(tmp_path / "c.md")
+    args = argparse.Namespace(counter_summary=[out, d], trace_command="rocprofv3 ...")
+    bench.counter_summary(args, PRESETS["llama7b_e16r64k4"])
+    assert "| SQ_WAVES | 40 | 2 | `q1` |" in open(out).read()
