@@ -901,6 +901,33 @@ def test_calls_run_in_order_on_the_callers_streams():
         m.destroy()
 
 
+def test_model_table_upload_is_ordered_on_its_stream():
+    """ada_model_create uploads the work table asynchronously on the stream it is given:
+    a merge enqueued right after it on that stream (no host synchronisation between
+    them) sees the whole table.  Many small projections make the table large (tens of
+    KB per tile class), and a kernel queued ahead on the stream delays the upload."""
+    E, r, k = 4, 16, 2
+    banks = [synth.adapter_bank(1700 + i, E, r, 8 * (1 + i % 9), 8 * (1 + (5 * i) % 11), "bf16") for i in range(600)]
+    idx, gate = make_selection(E, k, 64, "bf16", 23)
+    ws = [W.to(DEV) for W, _, _ in banks]
+    dev = [(w, None, Aw.to(DEV), Bw.to(DEV)) for w, (_, Aw, Bw) in zip(ws, banks)]
+    didx, dgate = idx.to(DEV), gate.to(DEV)
+    big = torch.randn(1 << 26, device=DEV)
+    sync()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for _ in range(4):
+            big.mul_(1.0001)  # keep the stream busy when the upload is enqueued
+        m = A.AdaModel(dev, E, r, stream=st)
+        A.ada_merge(m, didx, dgate, 2.0, stream=st)
+    sync()
+    g64 = gate.numpy().astype(np.float64)
+    for w, (W, Aw, Bw) in zip(ws, banks):
+        check_close(w, O.merge(to64(W), to64(Aw), to64(Bw), idx.numpy(), g64, 2.0), *tol(torch.bfloat16),
+                    "merge right after an asynchronous table upload")
+    m.destroy()
+
+
 # ---------------------------------------------------------------- graph capture
 
 

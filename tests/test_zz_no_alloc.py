@@ -73,3 +73,39 @@ def test_static_layer_path_refuses_intermediates_beyond_its_array():
     assert lib.ada_lora_layer_static(arr, 1, 4, 8, idx, idx, 2, 2.0, ADA_BF16, None) == ADA_ESHAPE
     arr_ok_size = (AdaLoraProj * 1)(AdaLoraProj(P, P, P, P, None, 1024, 64, 64))
     assert lib.ada_lora_layer_static(arr_ok_size, 1, 4, 8, idx, idx, 2, 2.0, ADA_BF16, None) == _lib.ADA_EINVAL
+
+
+@pytest.mark.gpu
+def test_static_layer_path_replays_under_graph_capture():
+    """The callers it is for include code under HIP graph capture: captured once, the
+    call replays with the same results as eager calls, replay after replay, with eager
+    work on the same static array in between (a different layer shape each time)."""
+    E, r, k = 8, 16, 2
+    banks, xs = group(700, E, r, [(264, 520), (520, 264)], "bf16")
+    h, R = synth.small_router(7, E, 64, "bf16")
+    idx_np, g_np = O.pregate(to64(h), to64(R), k)
+    idx = torch.tensor(idx_np, dtype=torch.int32, device=DEV)
+    gate = torch.tensor(g_np, dtype=torch.float32, device=DEV)
+    dev = [tuple(t.to(DEV) for t in b) for b in banks]
+    xd = [x.to(DEV) for x in xs]
+    eager = [torch.empty(W.shape[0], dtype=torch.bfloat16, device=DEV) for W, _, _ in banks]
+    A.ada_lora_layer([(w, a, b, x, y) for (w, a, b), x, y in zip(dev, xd, eager)], idx, gate, 2.0)
+    ys = [torch.full_like(y, float("nan")) for y in eager]
+    call = [(w, a, b, x, y) for (w, a, b), x, y in zip(dev, xd, ys)]
+    A.ada_lora_layer_static(call, idx, gate, 2.0)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.ada_lora_layer_static(call, idx, gate, 2.0)
+    other, other_x = group(900, E, r, [(136, 1032)], "bf16")
+    o_dev = [tuple(t.to(DEV) for t in b) for b in other]
+    o_y = torch.empty(136, dtype=torch.bfloat16, device=DEV)
+    for rep in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        # eager use of the same static array between replays
+        A.ada_lora_layer_static([(o_dev[0][0], o_dev[0][1], o_dev[0][2], other_x[0].to(DEV), o_y)], idx, gate, 2.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, ys):
+            assert torch.equal(a, b), rep
