@@ -368,6 +368,49 @@ def test_merge_error_is_one_rounding(E, r, k, d_out, d_in):
     m2.destroy()
 
 
+COEF_CASES = [
+    # r, gates of the first selection, gates of the second (None: a merge, else a switch)
+    (64, [1.0, 1e-30, 0.5], None),                 # ratio 1e-30 between neighbours in |c| order
+    (64, [1e-39, 1.0], None),                      # a subnormal gate
+    (64, [0.25, 0.25, 0.25, 0.25], None),          # equal magnitudes: ties keep their order
+    (64, [0.7, 0.3], [0.3, 0.7]),                  # a switch: equal |c| with opposite signs
+    (128, [0.6, 0.4], [0.9, 0.1]),                 # two 64-deep chunks per slot
+    (32, [0.5, 0.3, 0.2], [0.6, 0.4]),             # rank 32: 32-deep chunks, one slot each
+    (64, [0.5, 0.3, 0.2], None),                   # three slots: a half-empty last pair of chunks
+]
+
+
+@pytest.mark.parametrize("r,g1,g2", COEF_CASES)
+def test_scaled_accumulators_on_extreme_and_tied_coefficients(r, g1, g2):
+    """Long contractions whose chunks each hold one slot keep B raw and rescale the fp32
+    accumulators between slots in order of increasing |c|: extreme ratios must neither
+    overflow nor lose the large slot, ties and opposite signs must not drop a slot, and
+    the result is the stated tolerance away from the exact merge (or switch)."""
+    E, d_out, d_in = 8, 136, 264
+    W, Aw, Bw = synth.adapter_bank(61 + r, E, r, d_out, d_in, "bf16")
+    i1 = torch.tensor([1, 4, 6, 0][:len(g1)], dtype=torch.int32)
+    t1 = torch.tensor(g1, dtype=torch.float32)
+    W64, A64, B64 = to64(W), to64(Aw), to64(Bw)
+    w = W.to(DEV)
+    m = A.AdaModel([(w, None, Aw.to(DEV), Bw.to(DEV))], E, r)
+    if g2 is None:
+        assert len(g1) * r > 64
+        ref = O.merge(W64, A64, B64, i1.numpy(), t1.numpy().astype(np.float64), 2.0)
+        A.ada_merge(m, i1.to(DEV), t1.to(DEV), 2.0)
+    else:
+        i2 = torch.tensor([2, 1, 7][:len(g2)], dtype=torch.int32)
+        t2 = torch.tensor(g2, dtype=torch.float32)
+        assert (len(g1) + len(g2)) * r > 64
+        ref = O.switch(W64, A64, B64, (i1.numpy(), t1.numpy().astype(np.float64)),
+                       (i2.numpy(), t2.numpy().astype(np.float64)), 2.0)
+        A.ada_switch(m, (i1.to(DEV), t1.to(DEV)), (i2.to(DEV), t2.to(DEV)), 2.0)
+    sync()
+    got = to64(w)
+    assert np.all(np.isfinite(got))
+    check_close(got, ref, BF16_RTOL, BF16_ATOL, f"scaled accumulators r={r} gates {g1} {g2}")
+    m.destroy()
+
+
 @pytest.mark.parametrize("E,r,k", [(8, 16, 2), (8, 16, 4), (16, 64, 4)])  # each tile class
 def test_stack_of_mixed_shapes_in_one_launch(E, r, k):
     """Several projections of different shapes in one model (one launch): every
