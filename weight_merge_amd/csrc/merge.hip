@@ -36,7 +36,12 @@
 //     (each tile row a 512-byte run of W; 2.6% faster on the 7B stack than 64 x 128),
 //     up to k*r = 64 it is 64 x 128 (half the A_cat columns to gather: the fused
 //     switch at k*r = 64 runs 8% slower on 32 x 256).  Long contractions use 128 x 128
-//     tiles so each gathered adapter byte serves more weights.
+//     tiles so each gathered adapter byte serves more weights.  Their latency (one L2
+//     round trip per chunk, the W tile's HBM latency) is hidden by other workgroups
+//     of the CU rather than inside one: at 64-deep chunks on scaled accumulators a
+//     lean form (one operand buffer, W loaded only for the last chunk, the delta
+//     through LDS in halves) fits three workgroups per CU where the double-buffered
+//     form fits two, and is 8% faster on the 7B rank-64 stack.
 //   * Workgroup ids are remapped so each XCD walks a contiguous range of tiles,
 //     keeping a projection's adapter rows and columns in that XCD's L2.
 #include "common.h"
@@ -253,17 +258,22 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 //   3: r a power of two and a multiple of KC: every chunk lies inside one slot, so the
 //      slot, its coefficient and its base addresses are uniform per chunk
 // LONG marks the long-contraction instantiations (k*r > 64: 128 x 128 tiles): they ask
-// for two waves per SIMD and defer the gather masks (step 4); with RMODE 3 they use
-// the scaled accumulators, otherwise the split fold.
+// for two waves per SIMD (three in the lean form, NBUF = 1) and defer the gather masks
+// (step 4); with RMODE 3 they use the scaled accumulators, otherwise the split fold.
 #ifndef ADA_WAVES_PER_EU
 #define ADA_WAVES_PER_EU 1
 #endif
 template <int KC, int RB, int CT, int WGN, int RMODE, bool LONG, int NBUF>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LONG ? 2 : ADA_WAVES_PER_EU, 8)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LONG ? (NBUF == 1 ? 3 : 2) : ADA_WAVES_PER_EU, 8)))
 merge_bf16_kernel(MergeParams p) {
   constexpr int WGM = 4 / WGN;
   constexpr int BM = 16 * RB * WGM, BN = 16 * CT * WGN;
   constexpr bool kAccScale = LONG && RMODE == 3;  // coefficients on the fp32 accumulators
+  // lean form of a long contraction (one operand buffer): W is loaded for the last
+  // chunk and the delta passes through LDS in two halves, so a workgroup takes ~40 KB
+  // and <= 168 VGPRs and three share a CU
+  constexpr bool kLean = LONG && NBUF == 1;
+  static_assert(!kLean || RMODE == 3, "the lean form runs on scaled accumulators");
   constexpr bool kSplit = !kAccScale;             // coefficients folded into B as a bf16 pair
   constexpr int NPL = kSplit ? 2 : 1;             // B planes per buffer
   constexpr int LDB = KC + 8;   // B plane row pitch (elements)
@@ -286,7 +296,7 @@ merge_bf16_kernel(MergeParams p) {
   constexpr int LDD = BN + 4;  // delta row pitch (floats): 16 rows of a 16-byte column write hit 64 banks
   constexpr int BPLANE = BM * LDB;
   constexpr int STAGE_BYTES = NBUF * (NPL * BPLANE + KC * LDA) * 2;
-  constexpr int DELTA_BYTES = BM * LDD * 4;
+  constexpr int DELTA_BYTES = (kLean ? BM / 2 : BM) * LDD * 4;
   constexpr int SMEM = STAGE_BYTES > DELTA_BYTES ? STAGE_BYTES : DELTA_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   uint16_t (*Bs)[NPL * BPLANE] = reinterpret_cast<uint16_t (*)[NPL * BPLANE]>(smem);
@@ -345,8 +355,10 @@ merge_bf16_kernel(MergeParams p) {
   auto w_ok = [&](int u) { return row_t + kRowStep * u < T.d_out && col_t < T.d_in; };
   auto w_off = [&](int u) { return w_ok(u) ? woff0 + uint32_t(u) * wstep : 0u; };  // out of range: W[0][0..8)
   u32x4 wv[NV];
+  if constexpr (!kLean) {
 #pragma unroll
-  for (int u = 0; u < NV; ++u) wv[u] = load16_stream(src, w_off(u));
+    for (int u = 0; u < NV; ++u) wv[u] = load16_stream(src, w_off(u));
+  }
 
   // 3. active slots, in selection order: index in range and coefficient nonzero
   if (wave == 0) {
@@ -396,6 +408,10 @@ merge_bf16_kernel(MergeParams p) {
   if (nslot == 0) {
     // Nothing selected: in place there is nothing to write; out of place, copy.
     if (T.src == T.dst) return;
+    if constexpr (kLean) {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) wv[u] = load16_stream(src, w_off(u));
+    }
 #pragma unroll
     for (int u = 0; u < NV; ++u)
       if (w_ok(u)) store16_stream(dst, w_off(u), wv[u]);
@@ -650,6 +666,74 @@ merge_bf16_kernel(MergeParams p) {
   stage_load(0);
   stage_store(0);
   __syncthreads();
+  if constexpr (kLean) {
+    // 4'. one operand buffer: chunk c+1 waits in registers until every wave has read
+    // chunk c (a second barrier per chunk, for half the operand LDS)
+    for (int c = 0; c + 1 < nchunks; ++c) {
+      stage_load((c + 1) * KC);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk(0);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      stage_store(0);
+      rescale(c);
+      __syncthreads();
+    }
+    // W for the epilogue goes out now, into the registers the operand staging no
+    // longer needs; its HBM latency overlaps the last chunk here and the other two
+    // workgroups of the CU.  Its offsets, and the delta's, are recomputed from a
+    // thread index the compiler cannot see through (the empty asm): hoisted to the
+    // kernel's start they would stay live across the K loop and spill.
+    int tid_l = tid;
+    asm volatile("" : "+v"(tid_l));
+    const int row_l = T.row0 + tid_l / (BN / 8);
+    const int col_l = T.col0 + 8 * (tid_l % (BN / 8));
+    const uint32_t woff_l = 2u * (uint32_t(row_l) * uint32_t(T.ld) + uint32_t(col_l));
+    auto wl_ok = [&](int u) { return row_l + kRowStep * u < T.d_out && col_l < T.d_in; };
+    auto wl_off = [&](int u) { return wl_ok(u) ? woff_l + uint32_t(u) * wstep : 0u; };
+#pragma unroll
+    for (int u = 0; u < NV; ++u) wv[u] = load16_stream(src, wl_off(u));
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_chunk(0);
+
+    // 5'. the delta in two halves of BM / 2 rows (WGM = 2 row groups of waves): the
+    // waves of group h write theirs, then every thread finishes its W vectors of those
+    // rows (vectors u < NV / 2 lie in the first half)
+    static_assert(WGM == 2 && NV % 2 == 0 && (NV / 2) * kRowStep == BM / 2, "two row halves");
+    const float cl = s_coef[nslot - 1];
+    const int q_l = (tid_l & 63) >> 4, li_l = tid_l & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();  // every wave is done reading the operand chunk, then the first half
+      if (wy == h) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int row = 16 * RB * wy + 16 * rb + li_l - h * (BM / 2);
+            const int col = 16 * CT * wx + 32 * (ct >> 1) + 8 * q_l + 4 * (ct & 1);
+            *reinterpret_cast<f32x4*>(&Ds[row * LDD + col]) = acc[rb][ct];
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = h * (NV / 2); u < (h + 1) * (NV / 2); ++u) {
+        if (!wl_ok(u)) continue;
+        const int v = tid_l + 256 * u;
+        const float* d = &Ds[(v / (BN / 8) - h * (BM / 2)) * LDD + 8 * (v % (BN / 8))];
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(d);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(d + 4);
+        const u32x4 w = wv[u];
+        u32x4 o;
+        o.x = pack_bf16x2(fmaf(d0[0], cl, bf16_lo(w.x)), fmaf(d0[1], cl, bf16_hi(w.x)));
+        o.y = pack_bf16x2(fmaf(d0[2], cl, bf16_lo(w.y)), fmaf(d0[3], cl, bf16_hi(w.y)));
+        o.z = pack_bf16x2(fmaf(d1[0], cl, bf16_lo(w.z)), fmaf(d1[1], cl, bf16_hi(w.z)));
+        o.w = pack_bf16x2(fmaf(d1[2], cl, bf16_lo(w.w)), fmaf(d1[3], cl, bf16_hi(w.w)));
+        store16_stream(dst, wl_off(u), o);
+      }
+    }
+    return;
+  }
   if constexpr (NBUF == 1) {
     // the launch's contraction fits one chunk (the host picks this form only then)
     mfma_chunk(0);
@@ -832,14 +916,15 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t
     // SIMD in registers: the fused switch at k*r = 64 ran 30% slower with it)
     // k*r <= 32 is a single chunk (one operand buffer); long contractions whose rank is a
     // power-of-two multiple of 64 run 64-deep chunks, one slot each, on scaled
-    // accumulators, and the other long ones 32-deep chunks (scaled accumulators again
-    // at rank 32; otherwise the split fold, whose second B plane needs the room)
+    // accumulators, in the lean form (one operand buffer, three workgroups per CU), and
+    // the other long ones 32-deep chunks (scaled accumulators again at rank 32;
+    // otherwise the split fold, whose second B plane needs the room)
     switch (bf16_tile_class(kr_max)) {
       case 0: launch_bf16<32, NarrowTile, false, 1>(p, grid, block, s); break;
       case 1: launch_bf16<32, ShortTile, false, 2>(p, grid, block, s); break;
       default:
         if (p.r_shift >= 0 && p.r % 64 == 0)
-          hipLaunchKernelGGL((merge_bf16_kernel<64, LongTile::rb, LongTile::ct, LongTile::wgn, 3, true, 2>), grid,
+          hipLaunchKernelGGL((merge_bf16_kernel<64, LongTile::rb, LongTile::ct, LongTile::wgn, 3, true, 1>), grid,
                              block, 0, s, p);
         else
           launch_bf16<32, LongTile, true, 2>(p, grid, block, s);
