@@ -38,10 +38,10 @@
 //     switch at k*r = 64 runs 8% slower on 32 x 256).  Long contractions use 128 x 128
 //     tiles so each gathered adapter byte serves more weights.  Their latency (one L2
 //     round trip per chunk, the W tile's HBM latency) is hidden by other workgroups
-//     of the CU rather than inside one: at 64-deep chunks on scaled accumulators a
-//     lean form (one operand buffer, W loaded only for the last chunk, the delta
-//     through LDS in halves) fits three workgroups per CU where the double-buffered
-//     form fits two, and is 8% faster on the 7B rank-64 stack.
+//     of the CU rather than inside one: a lean form (one operand buffer, W loaded only
+//     for the last chunk, the delta through LDS in halves) fits three workgroups per CU
+//     where the double-buffered form fits two, and is 8-10% faster on the 7B stack at
+//     every long contraction measured (ranks 8 to 64, k*r 128 to 256).
 //   * Workgroup ids are remapped so each XCD walks a contiguous range of tiles,
 //     keeping a projection's adapter rows and columns in that XCD's L2.
 #include "common.h"
@@ -258,22 +258,22 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 //   3: r a power of two and a multiple of KC: every chunk lies inside one slot, so the
 //      slot, its coefficient and its base addresses are uniform per chunk
 // LONG marks the long-contraction instantiations (k*r > 64: 128 x 128 tiles): they ask
-// for two waves per SIMD (three in the lean form, NBUF = 1) and defer the gather masks
+// for two waves per SIMD (three or four in the lean form, NBUF = 1) and defer the gather masks
 // (step 4); with RMODE 3 they use the scaled accumulators, otherwise the split fold.
 #ifndef ADA_WAVES_PER_EU
 #define ADA_WAVES_PER_EU 1
 #endif
 template <int KC, int RB, int CT, int WGN, int RMODE, bool LONG, int NBUF>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LONG ? (NBUF == 1 ? 3 : 2) : ADA_WAVES_PER_EU, 8)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LONG ? (NBUF == 1 ? (KC == 32 && RMODE == 3 ? 4 : 3) : 2) : ADA_WAVES_PER_EU, 8)))
 merge_bf16_kernel(MergeParams p) {
   constexpr int WGM = 4 / WGN;
   constexpr int BM = 16 * RB * WGM, BN = 16 * CT * WGN;
   constexpr bool kAccScale = LONG && RMODE == 3;  // coefficients on the fp32 accumulators
   // lean form of a long contraction (one operand buffer): W is loaded for the last
-  // chunk and the delta passes through LDS in two halves, so a workgroup takes ~40 KB
-  // and <= 168 VGPRs and three share a CU
+  // chunk and the delta passes through LDS in two halves, so a workgroup takes 35-40 KB
+  // and <= 168 VGPRs and three share a CU (four at 32-deep chunks on scaled
+  // accumulators, which fit 128 VGPRs: 5-7% faster than three at rank 32)
   constexpr bool kLean = LONG && NBUF == 1;
-  static_assert(!kLean || RMODE == 3, "the lean form runs on scaled accumulators");
   constexpr bool kSplit = !kAccScale;             // coefficients folded into B as a bf16 pair
   constexpr int NPL = kSplit ? 2 : 1;             // B planes per buffer
   constexpr int LDB = KC + 8;   // B plane row pitch (elements)
@@ -700,7 +700,7 @@ merge_bf16_kernel(MergeParams p) {
     // waves of group h write theirs, then every thread finishes its W vectors of those
     // rows (vectors u < NV / 2 lie in the first half)
     static_assert(WGM == 2 && NV % 2 == 0 && (NV / 2) * kRowStep == BM / 2, "two row halves");
-    const float cl = s_coef[nslot - 1];
+    const float cl = kAccScale ? s_coef[nslot - 1] : 1.f;
     const int q_l = (tid_l & 63) >> 4, li_l = tid_l & 15;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -725,10 +725,17 @@ merge_bf16_kernel(MergeParams p) {
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(d + 4);
         const u32x4 w = wv[u];
         u32x4 o;
-        o.x = pack_bf16x2(fmaf(d0[0], cl, bf16_lo(w.x)), fmaf(d0[1], cl, bf16_hi(w.x)));
-        o.y = pack_bf16x2(fmaf(d0[2], cl, bf16_lo(w.y)), fmaf(d0[3], cl, bf16_hi(w.y)));
-        o.z = pack_bf16x2(fmaf(d1[0], cl, bf16_lo(w.z)), fmaf(d1[1], cl, bf16_hi(w.z)));
-        o.w = pack_bf16x2(fmaf(d1[2], cl, bf16_lo(w.w)), fmaf(d1[3], cl, bf16_hi(w.w)));
+        if constexpr (kAccScale) {
+          o.x = pack_bf16x2(fmaf(d0[0], cl, bf16_lo(w.x)), fmaf(d0[1], cl, bf16_hi(w.x)));
+          o.y = pack_bf16x2(fmaf(d0[2], cl, bf16_lo(w.y)), fmaf(d0[3], cl, bf16_hi(w.y)));
+          o.z = pack_bf16x2(fmaf(d1[0], cl, bf16_lo(w.z)), fmaf(d1[1], cl, bf16_hi(w.z)));
+          o.w = pack_bf16x2(fmaf(d1[2], cl, bf16_lo(w.w)), fmaf(d1[3], cl, bf16_hi(w.w)));
+        } else {
+          o.x = pack_bf16x2(bf16_lo(w.x) + d0[0], bf16_hi(w.x) + d0[1]);
+          o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
+          o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
+          o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
+        }
         store16_stream(dst, wl_off(u), o);
       }
     }
@@ -914,11 +921,10 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t
     // the caller built p's work table for the tile class of kr_max
     // short contractions loop over 32-deep chunks (a 64-deep chunk costs a wave per
     // SIMD in registers: the fused switch at k*r = 64 ran 30% slower with it)
-    // k*r <= 32 is a single chunk (one operand buffer); long contractions whose rank is a
-    // power-of-two multiple of 64 run 64-deep chunks, one slot each, on scaled
-    // accumulators, in the lean form (one operand buffer, three workgroups per CU), and
-    // the other long ones 32-deep chunks (scaled accumulators again at rank 32;
-    // otherwise the split fold, whose second B plane needs the room)
+    // k*r <= 32 is a single chunk (one operand buffer); long contractions run in the lean
+    // form (one operand buffer, three workgroups per CU): 64-deep chunks, one slot each,
+    // on scaled accumulators when the rank is a power-of-two multiple of 64, else
+    // 32-deep chunks (scaled accumulators again at rank 32; otherwise the split fold)
     switch (bf16_tile_class(kr_max)) {
       case 0: launch_bf16<32, NarrowTile, false, 1>(p, grid, block, s); break;
       case 1: launch_bf16<32, ShortTile, false, 2>(p, grid, block, s); break;
@@ -927,7 +933,7 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int kr_max, hipStream_t
           hipLaunchKernelGGL((merge_bf16_kernel<64, LongTile::rb, LongTile::ct, LongTile::wgn, 3, true, 1>), grid,
                              block, 0, s, p);
         else
-          launch_bf16<32, LongTile, true, 2>(p, grid, block, s);
+          launch_bf16<32, LongTile, true, 1>(p, grid, block, s);
         break;
     }
   } else {
