@@ -274,6 +274,7 @@ merge_bf16_kernel(MergeParams p) {
   // and <= 168 VGPRs and three share a CU (four at 32-deep chunks on scaled
   // accumulators, which fit 128 VGPRs: 5-7% faster than three at rank 32)
   constexpr bool kLean = LONG && NBUF == 1;
+  static_assert(!LONG || kLean, "long contractions run in the lean form");
   constexpr bool kSplit = !kAccScale;             // coefficients folded into B as a bf16 pair
   constexpr int NPL = kSplit ? 2 : 1;             // B planes per buffer
   constexpr int LDB = KC + 8;   // B plane row pitch (elements)
@@ -668,7 +669,12 @@ merge_bf16_kernel(MergeParams p) {
   __syncthreads();
   if constexpr (kLean) {
     // 4'. one operand buffer: chunk c+1 waits in registers until every wave has read
-    // chunk c (a second barrier per chunk, for half the operand LDS)
+    // chunk c (a second barrier per chunk, for half the operand LDS).  The last chunk
+    // is peeled off the loop, so every gather issued in the loop body is consumed in
+    // the same body (a load that could still be pending at the loop exit would make the
+    // compiler wait on it in the epilogue, and with it on the epilogue's stores), and
+    // the gathers are pinned ahead of the MFMAs (the scheduler would sink them to the
+    // end of the chunk to shorten their live ranges).
     for (int c = 0; c + 1 < nchunks; ++c) {
       stage_load((c + 1) * KC);
       __builtin_amdgcn_sched_barrier(0);
@@ -744,24 +750,6 @@ merge_bf16_kernel(MergeParams p) {
   if constexpr (NBUF == 1) {
     // the launch's contraction fits one chunk (the host picks this form only then)
     mfma_chunk(0);
-  } else if constexpr (kDefer) {
-    // Long contractions: the last chunk is peeled off the loop, so every gather
-    // issued in the loop body is consumed in the same body (a load that could still
-    // be pending at the loop exit would make the compiler wait on it in the
-    // epilogue, and with it on the epilogue's stores), and the gathers are pinned
-    // ahead of the MFMAs (the scheduler would sink them to the end of the chunk to
-    // shorten their live ranges).
-    for (int c = 0; c + 1 < nchunks; ++c) {
-      const int buf = c & 1;
-      stage_load((c + 1) * KC);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_chunk(buf);
-      __builtin_amdgcn_sched_barrier(0);
-      stage_store(buf ^ 1);
-      rescale(c);
-      __syncthreads();
-    }
-    mfma_chunk((nchunks - 1) & 1);
   } else {
     for (int c = 0; c < nchunks; ++c) {
       const int buf = c & 1;
@@ -777,9 +765,8 @@ merge_bf16_kernel(MergeParams p) {
 
   // 5. delta through LDS into the row-major layout of the W vectors: lane (q, i) of
   //    block (rb, ct) holds 4 adjacent columns of one row (a 16-byte write); then
-  //    W + delta is rounded once and stored (with scaled accumulators the delta is
-  //    first multiplied by the last slot's coefficient, in the same fma)
-  const float cl = kAccScale ? s_coef[nslot - 1] : 1.f;
+  //    W + delta is rounded once and stored (short contractions: the split fold has
+  //    already applied the coefficients)
   __syncthreads();  // every wave is done reading the operand chunks the delta overwrites
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -799,17 +786,10 @@ merge_bf16_kernel(MergeParams p) {
     const f32x4 d1 = *reinterpret_cast<const f32x4*>(d + 4);
     const u32x4 w = wv[u];
     u32x4 o;
-    if constexpr (kAccScale) {
-      o.x = pack_bf16x2(fmaf(d0[0], cl, bf16_lo(w.x)), fmaf(d0[1], cl, bf16_hi(w.x)));
-      o.y = pack_bf16x2(fmaf(d0[2], cl, bf16_lo(w.y)), fmaf(d0[3], cl, bf16_hi(w.y)));
-      o.z = pack_bf16x2(fmaf(d1[0], cl, bf16_lo(w.z)), fmaf(d1[1], cl, bf16_hi(w.z)));
-      o.w = pack_bf16x2(fmaf(d1[2], cl, bf16_lo(w.w)), fmaf(d1[3], cl, bf16_hi(w.w)));
-    } else {
-      o.x = pack_bf16x2(bf16_lo(w.x) + d0[0], bf16_hi(w.x) + d0[1]);
-      o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
-      o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
-      o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
-    }
+    o.x = pack_bf16x2(bf16_lo(w.x) + d0[0], bf16_hi(w.x) + d0[1]);
+    o.y = pack_bf16x2(bf16_lo(w.y) + d0[2], bf16_hi(w.y) + d0[3]);
+    o.z = pack_bf16x2(bf16_lo(w.z) + d1[0], bf16_hi(w.z) + d1[1]);
+    o.w = pack_bf16x2(bf16_lo(w.w) + d1[2], bf16_hi(w.w) + d1[3]);
     store16_stream(dst, w_off(u), o);
   }
 }
