@@ -219,8 +219,10 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 // col(ct, m) = 32 (ct / 2) + 8 (m / 4) + 4 (ct % 2) + m % 4 inside the wave's strip,
 // so lane (q, i) owns the columns 32 h + 8 q + [0, 8), h = 0 .. CT/2 - 1.
 //
-// Operands per K chunk of KC, in NBUF LDS buffers (two: chunk c+1 is stored while
-// chunk c is multiplied; one for launches whose contraction is a single chunk):
+// Operands per K chunk of KC, in NBUF LDS buffers (two for short contractions: chunk
+// c+1 is stored while chunk c is multiplied; one for a launch whose contraction is a
+// single chunk, and for the lean form of long contractions, whose chunk c+1 waits in
+// registers until every wave has read chunk c):
 //   As[k][col] = A_{e_j}[k - j r][col]               (rows of A_cat, as stored)
 //   B_cat rows, in one of two forms that both carry the coefficients c_j = +-s g_j
 //   at fp32 accuracy:
@@ -245,7 +247,8 @@ __device__ __forceinline__ TileRef find_tile(const MergeParams& p, int tile_rows
 //
 // Order of work inside a workgroup, chosen so HBM never waits on the rest:
 //   1. wave 0 loads the selection (k indices and gates, L2-resident);
-//   2. every lane issues its W loads (the tile's HBM traffic);
+//   2. every lane issues its W loads (the tile's HBM traffic; the lean form issues them
+//      at step 4's last chunk instead, to keep its registers for more workgroups);
 //   3. wave 0 compacts the active slots into LDS (waits for step 1 only);
 //   4. K chunks: gather chunk c+1 into registers while the MFMAs consume chunk c;
 //   5. W + delta is rounded once and stored.
