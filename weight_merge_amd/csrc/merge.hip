@@ -689,7 +689,7 @@ merge_bf16_kernel(MergeParams p) {
       __syncthreads();
     }
     // W for the epilogue goes out now, into the registers the operand staging no
-    // longer needs; its HBM latency overlaps the last chunk here and the other two
+    // longer needs; its HBM latency overlaps the last chunk here and the other
     // workgroups of the CU.  Its offsets, and the delta's, are recomputed from a
     // thread index the compiler cannot see through (the empty asm): hoisted to the
     // kernel's start they would stay live across the K loop and spill.
