@@ -40,7 +40,7 @@
 //     round trip per chunk, the W tile's HBM latency) is hidden by other workgroups
 //     of the CU rather than inside one: a lean form (one operand buffer, W loaded only
 //     for the last chunk, the delta through LDS in halves) fits three workgroups per CU
-//     where the double-buffered form fits two, and is 8-10% faster on the 7B stack at
+//     where the double-buffered form fits two, and is 7-13% faster on the 7B stack at
 //     every long contraction measured (ranks 8 to 64, k*r 128 to 256).
 //   * Workgroup ids are remapped so each XCD walks a contiguous range of tiles,
 //     keeping a projection's adapter rows and columns in that XCD's L2.
